@@ -1,0 +1,78 @@
+"""Exact-arithmetic definition of the row normalizations, for tiny rows.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+This is a second, independent statement of the same definitions as
+``oracle.c``, used to pin the fp64 oracle: sums, means and variances are
+exact rationals (``fractions.Fraction``), and the one square root is taken
+with ``decimal`` at 60 significant digits, so each returned value is the true
+result correctly rounded to a double (up to the 1e-60 relative error of the
+root).
+
+Definitions followed:
+  - RMSNorm (Emily.Fast docs, `rms_norm`; Emily notebook, Part 1 composed
+    cell): y_j = x_j / sqrt(mean_j(x_j^2) + eps) * w_j.
+  - LayerNorm (Emily.Fast docs, `layer_norm`): mean and (population) variance
+    of the row, y_j = (x_j - mean) / sqrt(var + eps) * w_j + b_j.
+
+Inputs are sequences of Python floats (every fp32 and bf16 value is an exact
+double) and eps is the exact double value of the fp32 the kernels receive.
+"""
+from __future__ import annotations
+
+from decimal import Decimal, localcontext
+from fractions import Fraction
+from typing import Sequence
+
+_DIGITS = 60
+
+
+def _to_decimal(q: Fraction) -> Decimal:
+    return Decimal(q.numerator) / Decimal(q.denominator)
+
+
+def _inv_sqrt(q: Fraction) -> Decimal:
+    """1 / sqrt(q) for a rational q > 0, to _DIGITS digits."""
+    return Decimal(1) / _to_decimal(q).sqrt()
+
+
+def rms_row(x: Sequence[float], w: Sequence[float], eps: float) -> list[float]:
+    n = len(x)
+    xs = [Fraction(v) for v in x]
+    mean_sq = sum(v * v for v in xs) / n
+    denom_sq = mean_sq + Fraction(eps)
+    with localcontext() as ctx:
+        ctx.prec = _DIGITS
+        if denom_sq == 0:
+            # 0/0: the IEEE result of the definition is NaN for every element.
+            return [float("nan")] * n
+        s = _inv_sqrt(denom_sq)
+        return [float(_to_decimal(xv * Fraction(wv)) * s) for xv, wv in zip(xs, w)]
+
+
+def layer_row(x: Sequence[float], w: Sequence[float], b: Sequence[float] | None,
+              eps: float) -> list[float]:
+    n = len(x)
+    xs = [Fraction(v) for v in x]
+    mean = sum(xs) / n
+    var = sum((v - mean) ** 2 for v in xs) / n
+    denom_sq = var + Fraction(eps)
+    bias = [Fraction(0)] * n if b is None else [Fraction(v) for v in b]
+    with localcontext() as ctx:
+        ctx.prec = _DIGITS
+        if denom_sq == 0:
+            return [float("nan")] * n
+        s = _inv_sqrt(denom_sq)
+        out = []
+        for xv, wv, bv in zip(xs, w, bias):
+            val = _to_decimal((xv - mean) * Fraction(wv)) * s + _to_decimal(bv)
+            out.append(float(val))
+        return out
+
+
+def rms(rows: Sequence[Sequence[float]], w, eps) -> list[list[float]]:
+    return [rms_row(r, w, eps) for r in rows]
+
+
+def layer(rows: Sequence[Sequence[float]], w, b, eps) -> list[list[float]]:
+    return [layer_row(r, w, b, eps) for r in rows]

@@ -1,0 +1,133 @@
+/*
+ * Reference oracle for the last-axis row normalizations.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, plainly written CPU
+ * definition that the HIP kernels are checked against.  Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg may load it.  It shares
+ * no code, header, table or helper with the HIP library, and includes no HIP
+ * header.  Every floating-point step is done in IEEE double.
+ *
+ * Sources (the pages the method is described on):
+ *  - "Fused transformer kernels on Emily" notebook, Part 1, the composed
+ *    RMSNorm cell: square, mean over the last axis, add eps, square root,
+ *    divide, multiply by the weight.
+ *  - Emily.Fast API docs, section `rms_norm`: x * rsqrt(mean(x^2, last axis)
+ *    + eps) * weight, weight of shape {width} broadcast over leading dims.
+ *  - Emily.Fast API docs, section `layer_norm`: mean and variance of the last
+ *    axis, then (x - mean) / sqrt(var + eps) * weight + bias.
+ *  - mlx-c-rust `compile/norm_fusion.rs`, module docs and the dual head-norm
+ *    graph builder: two independent RMS norms (queries with the query scale
+ *    weight, keys with the key scale weight), one shared eps, outputs in the
+ *    order queries then keys.
+ *
+ * Readings taken where the pages are silent:
+ *  - The variance divides by the width (population variance), matching a
+ *    Welford accumulator's M2 / n.
+ *  - eps is used exactly as the fp32 value the caller passes, widened to
+ *    double.
+ *  - No intermediate rounding: the result is the exact-as-double value; the
+ *    comparison with a bf16 or fp32 output happens in the tests.
+ *  - A NULL bias means a zero bias.
+ *
+ * Element types: 0 = IEEE binary32, 1 = bfloat16 (the upper 16 bits of a
+ * binary32).  Both widen to double without rounding.
+ *
+ * parity pins: every function here is pinned by the CPU tests (closed-form
+ * hand cases, exact rational brute force, invariants, special cases).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* Widen element i of a buffer of the given element type to double. */
+static double widen(const void *p, int dtype, int64_t i)
+{
+    if (dtype == ORACLE_F32) {
+        const float *f = (const float *)p;
+        return (double)f[i];
+    }
+    /* bfloat16: the stored 16 bits are the high half of a binary32. */
+    const uint16_t *h = (const uint16_t *)p;
+    uint32_t bits = ((uint32_t)h[i]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/*
+ * RMSNorm of each row (Emily.Fast docs, `rms_norm`; Emily notebook, Part 1):
+ *   ms  = (sum_j x_j^2) / N
+ *   y_j = x_j / sqrt(ms + eps) * w_j
+ * x: rows*width elements, w: width elements, y: rows*width doubles.
+ */
+void oracle_rms(const void *x, const void *w, int dtype, int64_t rows,
+                int64_t width, float eps, double *y)
+{
+    const double e = (double)eps;
+    for (int64_t r = 0; r < rows; ++r) {
+        double sum_sq = 0.0;
+        for (int64_t j = 0; j < width; ++j) {
+            double v = widen(x, dtype, r * width + j);
+            sum_sq += v * v;
+        }
+        double mean_sq = sum_sq / (double)width;
+        double root = sqrt(mean_sq + e);
+        for (int64_t j = 0; j < width; ++j) {
+            double v = widen(x, dtype, r * width + j);
+            y[r * width + j] = v / root * widen(w, dtype, j);
+        }
+    }
+}
+
+/*
+ * LayerNorm of each row (Emily.Fast docs, `layer_norm`):
+ *   mean = (sum_j x_j) / N
+ *   var  = (sum_j (x_j - mean)^2) / N
+ *   y_j  = (x_j - mean) / sqrt(var + eps) * w_j + b_j
+ * The variance is taken in a second pass over the row, around the mean of
+ * the first pass.  b may be NULL, which means zeros.
+ */
+void oracle_layer(const void *x, const void *w, const void *b, int dtype,
+                  int64_t rows, int64_t width, float eps, double *y)
+{
+    const double e = (double)eps;
+    for (int64_t r = 0; r < rows; ++r) {
+        double sum = 0.0;
+        for (int64_t j = 0; j < width; ++j)
+            sum += widen(x, dtype, r * width + j);
+        double mean = sum / (double)width;
+
+        double sum_dev_sq = 0.0;
+        for (int64_t j = 0; j < width; ++j) {
+            double d = widen(x, dtype, r * width + j) - mean;
+            sum_dev_sq += d * d;
+        }
+        double var = sum_dev_sq / (double)width;
+        double root = sqrt(var + e);
+
+        for (int64_t j = 0; j < width; ++j) {
+            double d = widen(x, dtype, r * width + j) - mean;
+            double bias = b ? widen(b, dtype, j) : 0.0;
+            y[r * width + j] = d / root * widen(w, dtype, j) + bias;
+        }
+    }
+}
+
+/*
+ * Dual-output query/key head RMSNorm (mlx-c-rust `compile/norm_fusion.rs`):
+ * the queries, viewed as q_rows head vectors of head_dim, are RMS-normalized
+ * with the query scale weight; the keys, k_rows head vectors, with the key
+ * scale weight; both with the same eps.  Outputs: queries into qy, keys into
+ * ky.
+ */
+void oracle_dual_head_rms(const void *q, const void *k, const void *qw,
+                          const void *kw, int dtype, int64_t q_rows,
+                          int64_t k_rows, int64_t head_dim, float eps,
+                          double *qy, double *ky)
+{
+    oracle_rms(q, qw, dtype, q_rows, head_dim, eps, qy);
+    oracle_rms(k, kw, dtype, k_rows, head_dim, eps, ky);
+}

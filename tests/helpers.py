@@ -1,0 +1,106 @@
+"""Comparison helpers for the tests: dtype views, bf16 rounding of fp64
+reference values, ulp distance and the tolerance checks.
+
+Tolerances (fp32: relative error <= 1e-5; bf16: <= 1 ulp and <= 7.9e-3
+relative):
+  RMSNorm      |y - r| / |r|                 (0/0 counts as 0)
+  LayerNorm    |y - r| / max(|r|, |w_j|)     (a floor at the scale of one
+                                              normalized entry, since
+                                              (x - mean) * s * w + b can cancel)
+  bf16 also    ulp distance between y and RNE_bf16(r) <= 1 (for LayerNorm
+               where |r| >= |w_j|)
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+F32_REL_TOL = 1e-5
+BF16_REL_TOL = 2.0 ** -7      # 7.8125e-3 <= 7.9e-3
+BF16_MAX_ULP = 1
+
+
+def to_oracle_array(t: torch.Tensor) -> np.ndarray:
+    """Host numpy view the oracle takes: float32, or uint16 bf16 bits."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float32:
+        return t.numpy()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    raise TypeError(t.dtype)
+
+
+def widen(t: torch.Tensor) -> np.ndarray:
+    """A float32 or bf16 tensor as exact float64 numpy values."""
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def rne_bf16_bits(r: np.ndarray) -> np.ndarray:
+    """Round float64 values to bfloat16 (round to nearest, ties to even)
+    directly, without passing through float32; returns uint16 bit patterns."""
+    r = np.asarray(r, dtype=np.float64)
+    out = np.zeros(r.shape, dtype=np.float64)
+    finite = np.isfinite(r) & (r != 0)
+    m, e = np.frexp(r[finite])                # r = m * 2^e, 0.5 <= |m| < 1
+    # bf16 has 8 significant bits; its smallest quantum is 2^-133.
+    q_exp = np.maximum(e - 8, -133)
+    q = np.ldexp(1.0, q_exp)
+    out[finite] = np.rint(r[finite] / q) * q   # division by 2^k is exact
+    out[~finite] = r[~finite]
+    out32 = out.astype(np.float32)             # exact: out has <= 8 bits
+    bits = out32.view(np.uint32) >> 16
+    return bits.astype(np.uint16)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return to_oracle_array(t.to(torch.bfloat16) if t.dtype != torch.bfloat16 else t)
+
+
+def _ordered(bits: np.ndarray) -> np.ndarray:
+    """Map bf16 bit patterns to integers ordered like the values."""
+    b = bits.astype(np.int32)
+    neg = (b & 0x8000) != 0
+    return np.where(neg, -(b & 0x7FFF), b & 0x7FFF)
+
+
+def ulp_distance_bf16(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    return np.abs(_ordered(a_bits) - _ordered(b_bits))
+
+
+def rel_err(y: np.ndarray, r: np.ndarray, floor: np.ndarray | None = None) -> np.ndarray:
+    """|y - r| / max(|r|, floor), with 0/0 := 0 and matching NaNs := 0."""
+    denom = np.abs(r) if floor is None else np.maximum(np.abs(r), np.abs(floor))
+    diff = np.abs(y - r)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        e = np.where(diff == 0, 0.0, diff / denom)
+    both_nan = np.isnan(y) & np.isnan(r)
+    return np.where(both_nan, 0.0, e)
+
+
+def check(op: str, y: torch.Tensor, r: np.ndarray, w: torch.Tensor | None = None,
+          label: str = "") -> dict:
+    """Assert the tolerance for one output tensor against the fp64 oracle.
+    Returns the measured error figures."""
+    yd = widen(y).reshape(r.shape)
+    floor = None
+    if op == "layer":
+        floor = np.broadcast_to(widen(w), r.shape)
+    err = rel_err(yd, r, floor)
+    nan_mismatch = int(np.sum(np.isnan(yd) != np.isnan(r)))
+    out = {"max_rel": float(np.max(err)) if err.size else 0.0,
+           "max_abs": float(np.nanmax(np.abs(yd - r))) if err.size else 0.0,
+           "nan_mismatch": nan_mismatch}
+    assert nan_mismatch == 0, f"{label}: NaN positions differ ({nan_mismatch})"
+    if y.dtype == torch.float32:
+        assert out["max_rel"] <= F32_REL_TOL, f"{label}: fp32 rel err {out['max_rel']:.3e}"
+    else:
+        assert out["max_rel"] <= BF16_REL_TOL, f"{label}: bf16 rel err {out['max_rel']:.3e}"
+        ulps = ulp_distance_bf16(bf16_bits(y).reshape(r.shape), rne_bf16_bits(r))
+        if op == "layer":
+            mask = np.abs(r) >= np.abs(floor)
+            ulps = np.where(mask, ulps, 0)
+        finite = np.isfinite(r)
+        ulps = np.where(finite, ulps, 0)
+        out["max_ulp"] = int(ulps.max()) if ulps.size else 0
+        assert out["max_ulp"] <= BF16_MAX_ULP, f"{label}: bf16 ulp distance {out['max_ulp']}"
+    return out

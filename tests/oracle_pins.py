@@ -1,0 +1,243 @@
+"""Pins for the fp64 oracle: checks against facts fixed by the pages and by
+mathematics, independent of the oracle's own code.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError when the oracle
+is wrong.  ``tests/test_oracle.py`` runs them on the real oracle;
+``tests/test_oracle_mutants.py`` runs them on deliberately broken copies of
+``oracle.c`` and requires every mutant to fail at least one pin.
+
+What pins what:
+  golden hand cases      the pages' doc-example inputs evaluated exactly
+                         (tests/golden/hand_cases.json, exact rationals)
+  exact brute force      random tiny rows (widths 1..16, fp32 and bf16
+                         inputs, random weight/bias/eps) against
+                         oracle/exact_tiny.py
+  unit-RMS invariant     w = 1:  mean(y^2) = ms / (ms + eps)
+  LayerNorm moments      w = 1, b = 0:  mean(y) = 0, mean(y^2) = v / (v + eps)
+  library identities     eps = 0: RMS = sqrt(N) x / ||x||_2 (numpy norm),
+                         LayerNorm = population z-score (numpy mean/std)
+  special cases          zero row, constant row, width 1, NaN propagation
+  invariances            LayerNorm(x + c) = LayerNorm(x); RMS(a x) = RMS(x)
+  affine structure       y(w, b) = y(1, 0) * w + b, column-indexed weights
+  row independence       permuting rows permutes outputs, bitwise
+  bf16 decoding          hand-built bf16 bit patterns decode to the values
+                         the format defines
+  dual q/k               each half against exact brute force, queries first
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+from oracle import exact_tiny
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = os.path.join(HERE, "golden", "hand_cases.json")
+
+
+def f32(v):
+    return float(np.float32(v))
+
+
+def _bf16_from_f32(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 bit patterns (RNE), numpy only."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def _bf16_values(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _close(a, b, rtol, floor=None, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    scale = np.abs(b) if floor is None else np.maximum(np.abs(b), floor)
+    err = np.abs(a - b)
+    bad = err > rtol * scale
+    bad &= ~(np.isnan(a) & np.isnan(b))
+    assert not np.any(bad), f"{what}: max err {np.max(err):.3e} (rtol {rtol})"
+
+
+# --------------------------------------------------------------------------
+def pin_golden_hand_cases(o):
+    with open(GOLDEN) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        x = np.array(c["x"], dtype=np.float32)
+        w = np.array(c["w"], dtype=np.float32)
+        exp = np.array(c["y"], dtype=np.float64)
+        if c["op"] == "rms":
+            got = o.rms(x, w, c["eps_f32"])
+        else:
+            got = o.layer(x, w, np.array(c["b"], dtype=np.float32), c["eps_f32"])
+        _close(got, exp, 1e-14, floor=1e-300, what=c["name"])
+
+
+def _tiny_rows(rng, dtype, width, rows):
+    x = rng.standard_normal((rows, width)).astype(np.float32) * np.float32(rng.uniform(0.1, 5))
+    x += np.float32(rng.uniform(-3, 3))
+    w = rng.uniform(-2, 2, width).astype(np.float32)
+    b = rng.uniform(-1, 1, width).astype(np.float32)
+    if dtype == "bf16":
+        xb, wb, bb = _bf16_from_f32(x), _bf16_from_f32(w), _bf16_from_f32(b)
+        return (xb, wb, bb), (_bf16_values(xb), _bf16_values(wb), _bf16_values(bb))
+    return (x, w, b), (x.astype(np.float64), w.astype(np.float64), b.astype(np.float64))
+
+
+def pin_exact_bruteforce_rms(o):
+    rng = np.random.default_rng(101)
+    for width in range(1, 17):
+        for dtype in ("f32", "bf16"):
+            (x, w, _), (xv, wv, _) = _tiny_rows(rng, dtype, width, 3)
+            eps = f32(rng.choice([0.0, 1e-6, 1e-5, 0.5]))
+            got = o.rms(x, w, eps)
+            exp = np.array(exact_tiny.rms(xv.tolist(), wv.tolist(), eps))
+            _close(got, exp, 1e-13, floor=1e-300, what=f"rms width {width} {dtype}")
+
+
+def pin_exact_bruteforce_layer(o):
+    rng = np.random.default_rng(202)
+    for width in range(1, 17):
+        for dtype in ("f32", "bf16"):
+            for use_bias in (True, False):
+                (x, w, b), (xv, wv, bv) = _tiny_rows(rng, dtype, width, 3)
+                eps = f32(rng.choice([1e-6, 1e-5, 0.5]))
+                got = o.layer(x, w, b if use_bias else None, eps)
+                exp = np.array(exact_tiny.layer(xv.tolist(), wv.tolist(),
+                                                bv.tolist() if use_bias else None, eps))
+                floor = np.abs(wv) + (np.abs(bv) if use_bias else 0.0) + 1e-300
+                _close(got, exp, 1e-13, floor=floor, what=f"layer width {width} {dtype}")
+
+
+def pin_rms_unit_invariant(o):
+    rng = np.random.default_rng(303)
+    for eps in (0.3, 1e-6):
+        x = rng.uniform(-1, 1, (8, 64)).astype(np.float32)
+        y = o.rms(x, np.ones(64, np.float32), f32(eps))
+        ms = np.mean(x.astype(np.float64) ** 2, axis=1)
+        _close(np.mean(y ** 2, axis=1), ms / (ms + f32(eps)), 1e-12, what="unit RMS")
+
+
+def pin_layer_moments(o):
+    rng = np.random.default_rng(404)
+    for eps in (0.3, 1e-5):
+        x = (rng.standard_normal((8, 96)) * 2 + 5).astype(np.float32)
+        y = o.layer(x, np.ones(96, np.float32), np.zeros(96, np.float32), f32(eps))
+        v = np.var(x.astype(np.float64), axis=1)        # population variance
+        assert np.max(np.abs(np.mean(y, axis=1))) < 1e-12, "LayerNorm mean not 0"
+        _close(np.mean(y ** 2, axis=1), v / (v + f32(eps)), 1e-12, what="LN var")
+
+
+def pin_library_identities(o):
+    rng = np.random.default_rng(505)
+    x = rng.uniform(-2, 2, (6, 50)).astype(np.float32)
+    xd = x.astype(np.float64)
+    ones = np.ones(50, np.float32)
+    rms = o.rms(x, ones, 0.0)
+    ref = xd * np.sqrt(50) / np.linalg.norm(xd, axis=1, keepdims=True)
+    _close(rms, ref, 1e-13, what="RMS vs sqrt(N) x/||x||")
+    ln = o.layer(x, ones, None, 0.0)
+    z = (xd - xd.mean(axis=1, keepdims=True)) / xd.std(axis=1, keepdims=True)
+    _close(ln, z, 1e-12, floor=1.0, what="LayerNorm vs z-score")
+
+
+def pin_special_cases(o):
+    w = np.array([1.5, -0.5, 2.0, 0.25], np.float32)
+    b = np.array([0.1, 0.2, -0.3, 0.4], np.float32)
+    # zero row, eps > 0: RMS gives exact zeros
+    y = o.rms(np.zeros((1, 4), np.float32), w, f32(1e-6))
+    assert np.all(y == 0.0), "RMS of zero row"
+    # constant row: LayerNorm gives exactly the bias
+    y = o.layer(np.full((2, 4), 3.25, np.float32), w, b, f32(1e-5))
+    assert np.array_equal(y, np.broadcast_to(b.astype(np.float64), (2, 4))), "LN const row"
+    # width 1
+    x1 = np.array([[2.0], [-0.5]], np.float32)
+    y = o.rms(x1, np.array([3.0], np.float32), 0.25)
+    _close(y[:, 0], [2.0 / np.sqrt(4.25) * 3.0, -0.5 / np.sqrt(0.5) * 3.0], 1e-15, what="RMS w1")
+    y = o.layer(x1, np.array([3.0], np.float32), np.array([0.75], np.float32), 0.25)
+    assert np.all(y == 0.75), "LN width 1 gives the bias"
+    # NaN in one row poisons only that row
+    x = np.ones((3, 4), np.float32)
+    x[1, 2] = np.nan
+    for y in (o.rms(x, w, f32(1e-6)), o.layer(x, w, b, f32(1e-6))):
+        assert np.all(np.isnan(y[1])) and np.all(np.isfinite(y[[0, 2]])), "NaN propagation"
+    # zero row with eps = 0: 0/0 is NaN
+    y = o.rms(np.zeros((1, 4), np.float32), w, 0.0)
+    assert np.all(np.isnan(y)), "RMS 0/0"
+
+
+def pin_invariances(o):
+    rng = np.random.default_rng(606)
+    # multiples of 2^-10 in [-4, 4): adding 7 and scaling by 4 stay exact in fp32
+    x = (rng.integers(-4096, 4096, (5, 40)) / 1024.0).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, 40).astype(np.float32)
+    b = rng.uniform(-0.1, 0.1, 40).astype(np.float32)
+    y0 = o.layer(x, w, b, f32(1e-5))
+    y1 = o.layer(x + np.float32(7.0), w, b, f32(1e-5))
+    _close(y1, y0, 1e-12, floor=1.0, what="LN shift invariance")
+    r0 = o.rms(x, w, 0.0)
+    r1 = o.rms(x * np.float32(4.0), w, 0.0)
+    _close(r1, r0, 1e-14, floor=1e-300, what="RMS scale invariance")
+
+
+def pin_affine_structure(o):
+    rng = np.random.default_rng(707)
+    x = rng.standard_normal((4, 12)).astype(np.float32)
+    w = rng.uniform(-2, 2, 12).astype(np.float32)
+    b = rng.uniform(-1, 1, 12).astype(np.float32)
+    ones, zeros = np.ones(12, np.float32), np.zeros(12, np.float32)
+    _close(o.rms(x, w, f32(1e-6)), o.rms(x, ones, f32(1e-6)) * w, 1e-15, floor=1e-300,
+           what="RMS weight per column")
+    base = o.layer(x, ones, zeros, f32(1e-6))
+    _close(o.layer(x, w, b, f32(1e-6)), base * w + b, 1e-14, floor=1.0,
+           what="LN weight and bias per column")
+    # a NULL bias is the zero bias
+    assert np.array_equal(o.layer(x, w, None, f32(1e-6)), o.layer(x, w, zeros, f32(1e-6)))
+
+
+def pin_row_independence(o):
+    rng = np.random.default_rng(808)
+    x = rng.standard_normal((7, 33)).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, 33).astype(np.float32)
+    b = rng.uniform(-0.1, 0.1, 33).astype(np.float32)
+    perm = rng.permutation(7)
+    assert np.array_equal(o.rms(x[perm], w, f32(1e-6)), o.rms(x, w, f32(1e-6))[perm])
+    assert np.array_equal(o.layer(x[perm], w, b, f32(1e-6)), o.layer(x, w, b, f32(1e-6))[perm])
+
+
+def pin_bf16_decoding(o):
+    # sign | 8 exponent bits (bias 127) | 7 mantissa bits:
+    # 0x3F80 = +1.0, 0x4000 = +2.0, 0xC040 = -3.0, 0x4090 = +4.5, 0x3E20 = 0.15625
+    bits = np.array([[0x3F80, 0x4000, 0xC040, 0x4090, 0x3E20]], np.uint16)
+    vals = [1.0, 2.0, -3.0, 4.5, 0.15625]
+    wb = np.array([0x3F80, 0x3F00, 0x4000, 0xBF80, 0x3F80], np.uint16)   # 1, .5, 2, -1, 1
+    wv = [1.0, 0.5, 2.0, -1.0, 1.0]
+    got = o.rms(bits, wb, 0.0)
+    _close(got[0], exact_tiny.rms_row(vals, wv, 0.0), 1e-15, what="bf16 decode (rms)")
+    got = o.layer(bits, wb, wb, 0.0)
+    _close(got[0], exact_tiny.layer_row(vals, wv, wv, 0.0), 1e-14, floor=1.0,
+           what="bf16 decode (layer)")
+
+
+def pin_dual(o):
+    rng = np.random.default_rng(909)
+    for dtype in ("f32", "bf16"):
+        (q, qw, _), (qv, qwv, _) = _tiny_rows(rng, dtype, 8, 6)
+        (k, kw, _), (kv, kwv, _) = _tiny_rows(rng, dtype, 8, 2)
+        eps = f32(1e-6)
+        qy, ky = o.dual_head_rms(q.reshape(3, 2, 8), k.reshape(1, 2, 8), qw, kw, eps)
+        assert qy.shape == (3, 2, 8) and ky.shape == (1, 2, 8)
+        _close(qy.reshape(6, 8), exact_tiny.rms(qv.tolist(), qwv.tolist(), eps), 1e-13,
+               floor=1e-300, what=f"dual queries {dtype}")
+        _close(ky.reshape(2, 8), exact_tiny.rms(kv.tolist(), kwv.tolist(), eps), 1e-13,
+               floor=1e-300, what=f"dual keys {dtype}")
+
+
+PINS = [pin_golden_hand_cases, pin_exact_bruteforce_rms, pin_exact_bruteforce_layer,
+        pin_rms_unit_invariant, pin_layer_moments, pin_library_identities,
+        pin_special_cases, pin_invariances, pin_affine_structure, pin_row_independence,
+        pin_bf16_decoding, pin_dual]

@@ -1,0 +1,78 @@
+"""The pins have teeth: plausible mistakes planted in copies of the oracle's
+C source (on the CPU, in a temporary directory) must each fail a pin.
+
+Each mutant is one textual edit of ``oracle/oracle.c`` (a dropped term, a
+wrong sign, divisor, index or operand), compiled with gcc to a private
+shared library.  None of the edits reads out of bounds.
+"""
+import os
+import shutil
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "rms_divisor_n_minus_1": ("double mean_sq = sum_sq / (double)width;",
+                              "double mean_sq = sum_sq / (double)(width > 1 ? width - 1 : 1);"),
+    "rms_dropped_eps": ("double root = sqrt(mean_sq + e);", "double root = sqrt(mean_sq);"),
+    "rms_eps_outside_root": ("double root = sqrt(mean_sq + e);",
+                             "double root = sqrt(mean_sq) + e;"),
+    "rms_sum_not_squared": ("sum_sq += v * v;", "sum_sq += v * (v < 0 ? -v : v);"),
+    "rms_multiply_by_root": ("y[r * width + j] = v / root * widen(w, dtype, j);",
+                             "y[r * width + j] = v * root * widen(w, dtype, j);"),
+    "rms_weight_reversed": ("y[r * width + j] = v / root * widen(w, dtype, j);",
+                            "y[r * width + j] = v / root * widen(w, dtype, width - 1 - j);"),
+    "rms_no_weight": ("y[r * width + j] = v / root * widen(w, dtype, j);",
+                      "y[r * width + j] = v / root;"),
+    "layer_mean_divisor": ("double mean = sum / (double)width;",
+                           "double mean = sum / (double)(width + 1);"),
+    "layer_var_unbiased": ("double var = sum_dev_sq / (double)width;",
+                           "double var = sum_dev_sq / (double)(width > 1 ? width - 1 : 1);"),
+    "layer_dropped_eps": ("double root = sqrt(var + e);", "double root = sqrt(var);"),
+    "layer_bias_sign": ("y[r * width + j] = d / root * widen(w, dtype, j) + bias;",
+                        "y[r * width + j] = d / root * widen(w, dtype, j) - bias;"),
+    "layer_no_centering": ("double d = widen(x, dtype, r * width + j) - mean;\n"
+                           "            double bias",
+                           "double d = widen(x, dtype, r * width + j);\n"
+                           "            double bias"),
+    "layer_var_of_raw_x": ("sum_dev_sq += d * d;",
+                           "sum_dev_sq += (d + mean) * (d + mean);"),
+    "layer_bias_reversed": ("double bias = b ? widen(b, dtype, j) : 0.0;",
+                            "double bias = b ? widen(b, dtype, width - 1 - j) : 0.0;"),
+    "bf16_decode_shift": ("uint32_t bits = ((uint32_t)h[i]) << 16;",
+                          "uint32_t bits = ((uint32_t)h[i]) << 15;"),
+    "bf16_decode_low_half": ("uint32_t bits = ((uint32_t)h[i]) << 16;",
+                             "uint32_t bits = ((uint32_t)h[i]) << 16 | 0x8000u;"),
+    "dual_swapped_weights": ("oracle_rms(k, kw, dtype, k_rows, head_dim, eps, ky);",
+                             "oracle_rms(k, qw, dtype, k_rows, head_dim, eps, ky);"),
+    "dual_eps_dropped_for_keys": ("oracle_rms(k, kw, dtype, k_rows, head_dim, eps, ky);",
+                                  "oracle_rms(k, kw, dtype, k_rows, head_dim, 0.0f, ky);"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, source, name):
+    old, new = MUTANTS[name]
+    assert source.count(old) >= 1, f"mutation site for {name} not found"
+    src = tmp_path / "oracle_mutant.c"
+    src.write_text(source.replace(old, new, 1))
+    lib = oracle.build(str(src), str(tmp_path / f"lib_{name}.so"))
+    mutant = oracle.Oracle(lib)
+    failures = []
+    for pin in oracle_pins.PINS:
+        try:
+            pin(mutant)
+        except AssertionError as e:
+            failures.append(f"{pin.__name__}: {e}")
+    assert failures, f"mutant {name} passed every pin"
