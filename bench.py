@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused row normalizations on one MI355X.
+
+One step = one pass of the whole path over one batch of seeded synthetic
+input, inputs resident in HBM:
+  1. dual q/k head RMSNorm, bf16, q [4096,32,128] + k [4096,8,128], one launch
+  2. RMSNorm bf16 [16384, 8192]
+  3. LayerNorm bf16 [65536, 4096] (mean 3, 0.1% outliers x100), with bias
+
+Metric: achieved HBM GB/s over the algorithmic bytes (read x once, write y
+once, read the weights/bias once per launch) and rows/s.  Timing: W warm-up
+steps, then K steps bracketed by synchronize, HIP events recorded on the
+stream the kernels run on around every launch (per-kernel durations) and
+around the whole region.  The step order makes every input cold in the
+caches: 1.6 GB of other traffic separates two reads of the same tensor, more
+than the 256 MB MALL.
+
+Prints ONE JSON line.  Extra legs (outside the timed region): the 16-byte
+copy kernel over the LayerNorm's bytes (practical ceiling) and the fp64 CPU
+oracle over one step's rows (``cpu_baseline``).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_bf16_65536x4096_traffic.json")
+KERNEL_SOURCES = ["fnorm_device.hpp", "fnorm_kernels.hpp", "fnorm_instances.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "transformer_row_normalization_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--ops", default="dual,rms,layer", help="subset of the step, for profiling")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on one GPU only; "
+                          "rows shard across GPUs with no exchange, so the per-GPU kernel "
+                          "is what one GPU measures"}))
+        sys.exit(2)
+
+    import torch
+
+    import transformer_row_normalization_amd as trn
+    from transformer_row_normalization_amd import inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ops = args.ops.split(",")
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    log("[bench] generating inputs")
+    wl_dual = inputs.dual_bf16_4096tok()
+    wl_rms = inputs.rms_bf16_16384x8192()
+    wl_ln = inputs.layer_bf16_65536x4096()
+    d = {}
+    for wl in (wl_dual, wl_rms, wl_ln):
+        d[wl.name] = {k: v.to(dev) for k, v in wl.tensors.items() if torch.is_tensor(v)}
+    dq, drms, dln = d[wl_dual.name], d[wl_rms.name], d[wl_ln.name]
+    qy, ky = torch.empty_like(dq["q"]), torch.empty_like(dq["k"])
+    y_rms = torch.empty_like(drms["x"])
+    y_ln = torch.empty_like(dln["x"])
+
+    def nbytes(*ts):
+        return sum(t.numel() * t.element_size() for t in ts)
+
+    plan = []   # (name, launch fn, algorithmic bytes, rows, kernel description)
+    if "dual" in ops:
+        plan.append(("dual_bf16_q131072_k32768_hd128",
+                     lambda: trn.dual_head_rms_norm(dq["q"], dq["k"], dq["qw"], dq["kw"],
+                                                    wl_dual.eps, q_out=qy, k_out=ky),
+                     nbytes(dq["q"], dq["k"], dq["qw"], dq["kw"], qy, ky), wl_dual.rows,
+                     trn.describe(trn.OP_DUAL, trn.BF16, 128)))
+    if "rms" in ops:
+        plan.append(("rms_bf16_16384x8192",
+                     lambda: trn.rms_norm(drms["x"], drms["w"], wl_rms.eps, out=y_rms),
+                     nbytes(drms["x"], drms["w"], y_rms), wl_rms.rows,
+                     trn.describe(trn.OP_RMS, trn.BF16, 8192)))
+    if "layer" in ops:
+        plan.append(("layer_bf16_65536x4096",
+                     lambda: trn.layer_norm(dln["x"], dln["w"], dln["b"], wl_ln.eps, out=y_ln),
+                     nbytes(dln["x"], dln["w"], dln["b"], y_ln), wl_ln.rows,
+                     trn.describe(trn.OP_LAYER, trn.BF16, 4096)))
+
+    stream = torch.cuda.current_stream(dev)
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        for _, fn, _, _, _ in plan:
+            fn()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(plan) + 1)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for s in range(K):
+        evs[s][0].record(stream)
+        for i, (_, fn, _, _, _) in enumerate(plan):
+            fn()
+            evs[s][i + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K
+
+    per_op = {}
+    for i, (name, _, b, rows, kname) in enumerate(plan):
+        durs = sorted(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(K))
+        avg = sum(durs) / K
+        per_op[name] = {"kernel": kname, "bytes": b, "rows": rows,
+                        "avg_ms": round(avg, 5), "min_ms": round(durs[0], 5),
+                        "median_ms": round(durs[K // 2], 5),
+                        "gbs": round(b / (avg * 1e-3) / 1e9, 1),
+                        "frac_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                        "rows_per_s": round(rows / (avg * 1e-3), 1)}
+        log(f"[bench] {name}: {per_op[name]}")
+    step_bytes = sum(p[2] for p in plan)
+    step_rows = sum(p[3] for p in plan)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # practical ceiling: 16-byte copy kernel over the LayerNorm's byte count
+    ceiling = None
+    if "layer" in ops:
+        n = dln["x"].numel()
+        src, dst = dln["x"], y_ln
+        for _ in range(3):
+            trn.bench_copy(src, dst)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            trn.bench_copy(src, dst)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / reps
+        ceiling = {"kernel": "copy16 (fnorm_bench_copy)", "bytes": 2 * n * 2,
+                   "avg_ms": round(cms, 5),
+                   "gbs": round(2 * n * 2 / (cms * 1e-3) / 1e9, 1)}
+        log(f"[bench] copy ceiling: {ceiling}")
+
+    dominant = max(per_op, key=lambda k: per_op[k]["avg_ms"])
+    dom = per_op[dominant]
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == dominant:
+            traffic = tr.get("hbm_bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(dom["bytes"] / (dom["avg_ms"] * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(dom["bytes"] / (dom["avg_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "traffic": traffic, "kernel": dominant}
+
+    cpu = None
+    if not args.no_cpu_baseline and len(plan) == 3:
+        cpu = cpu_baseline(wl_dual, wl_rms, wl_ln, log)
+
+    out = {"metric": "achieved HBM GB/s (% of peak) and rows/sec for fused RMSNorm/LayerNorm",
+           "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic (seeded, shapes and distributions of the workloads)",
+           "config": {"workload": "step = " + " + ".join(p[0] for p in plan),
+                      "io_dtype": "bf16", "accumulate": "f32",
+                      "rows_per_step": step_rows, "bytes_per_step": step_bytes,
+                      "rows_per_s": round(step_rows / (ms_per_step * 1e-3), 1),
+                      "frac_peak_hbm": round(value / PEAK_HBM_GBS, 4),
+                      "parallelism": "rows across workgroups (1 GPU)"},
+           "per_op": per_op, "copy_ceiling": ceiling,
+           "roofline": roofline, "cpu_baseline": cpu,
+           "wall_s_timed_region": round(wall, 4)}
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl_dual, wl_rms, wl_ln, log):
+    """The fp64 oracle, as it stands, over one full step of the same inputs
+    (row chunks, single thread); reported in the metric's unit over the same
+    algorithmic bytes."""
+    import oracle
+    from tests import helpers
+
+    o = oracle.default()
+    log("[bench] cpu baseline (oracle, 1 thread, one full step)")
+    t = wl_dual.tensors
+    arr = {k: helpers.to_oracle_array(t[k]) for k in ("q", "k", "qw", "kw")}
+    total_bytes = 0
+    t0 = time.perf_counter()
+    o.dual_head_rms(arr["q"], arr["k"], arr["qw"], arr["kw"], wl_dual.eps)
+    total_bytes += sum(v.nbytes for v in arr.values()) + arr["q"].nbytes + arr["k"].nbytes
+    for wl, op in ((wl_rms, "rms"), (wl_ln, "layer")):
+        x = helpers.to_oracle_array(wl.tensors["x"])
+        w = helpers.to_oracle_array(wl.tensors["w"])
+        b = helpers.to_oracle_array(wl.tensors["b"]) if "b" in wl.tensors else None
+        for r0 in range(0, x.shape[0], 2048):
+            if op == "rms":
+                o.rms(x[r0:r0 + 2048], w, wl.eps)
+            else:
+                o.layer(x[r0:r0 + 2048], w, b, wl.eps)
+        total_bytes += 2 * x.nbytes + w.nbytes + (b.nbytes if b is not None else 0)
+    dt = time.perf_counter() - t0
+    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "one full step (all rows of the three workloads), fp64 C oracle, "
+                      "single thread, outputs in 2048-row chunks",
+            "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

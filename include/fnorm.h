@@ -1,0 +1,147 @@
+/*
+ * fnorm: fused last-axis row normalizations for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libfnorm.so.  Plain pointers and sizes only.
+ *
+ * Common conventions
+ * ------------------
+ *  - Tensors are contiguous, row-major [rows, width]; the normalization runs
+ *    over the last axis only (the fused kernels' contract in the
+ *    Emily.Bumblebee.FastKernels docs, "What's not rewritten": norms over any
+ *    other axis are not served).  rows is the product of the leading
+ *    dimensions.
+ *  - x, w, b and y are DEVICE pointers owned by the caller; they must stay
+ *    valid until the work queued on `stream` has completed.  The library
+ *    allocates nothing, frees nothing and never synchronizes.
+ *  - All tensors of one call share one element type `dtype` (fnorm_dtype);
+ *    the output has the input's type.  Arithmetic is fp32; a bf16 output is
+ *    the fp32 result rounded once, to nearest even.
+ *  - eps is fixed per call, must be finite and >= 0, and is added inside the
+ *    square root.
+ *  - `stream` is a hipStream_t; NULL means the null stream.  Calls return as
+ *    soon as the kernel is queued.
+ *  - y == x (in place) is allowed.  Any other overlap of an output with an
+ *    input or with another output is rejected with FNORM_ERR_ALIAS.
+ *  - Pointers that are not 16-byte aligned, and widths that are not a
+ *    multiple of 16 bytes, are served (by a scalar-access kernel), not
+ *    rejected.
+ *  - rows == 0 is a no-op that returns FNORM_OK (pointers may then be NULL).
+ *  - Every argument is validated before any HIP call; on an error nothing is
+ *    launched, the status is returned and fnorm_last_error() describes it.
+ *    Faults during execution surface on the stream, as for any kernel.
+ *  - Thread safety: no mutable global state except read-only caches of
+ *    device properties; the error text is per thread.
+ */
+#ifndef FNORM_H
+#define FNORM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FNORM_F32 = 0, FNORM_BF16 = 1 } fnorm_dtype;
+
+typedef enum {
+    FNORM_OK = 0,
+    FNORM_ERR_NULL = 1,        /* a required pointer is NULL while rows > 0 */
+    FNORM_ERR_SHAPE = 2,       /* rows < 0, width <= 0, or sizes overflow */
+    FNORM_ERR_EPS = 3,         /* eps negative, NaN or infinite */
+    FNORM_ERR_DTYPE = 4,       /* dtype not an fnorm_dtype */
+    FNORM_ERR_ALIAS = 5,       /* an output overlaps another buffer (other than y == x) */
+    FNORM_ERR_UNSUPPORTED = 6, /* no kernel for the request, or variant out of range */
+    FNORM_ERR_LAUNCH = 7       /* the HIP launch failed; fnorm_last_error() has the text */
+} fnorm_status;
+
+typedef enum { FNORM_OP_RMS = 0, FNORM_OP_LAYER = 1, FNORM_OP_DUAL = 2 } fnorm_op;
+
+/*
+ * RMSNorm (Emily.Fast docs, section `rms_norm`; the composed form is the
+ * Emily notebook's Part 1 RMSNorm cell):
+ *     y[r, j] = x[r, j] * rsqrt(mean_j(x[r, :]^2) + eps) * w[j]
+ * x, y: [rows, width]; w: [width], broadcast over rows.
+ */
+int fnorm_rms(const void* x, const void* w, void* y, int64_t rows, int64_t width, float eps,
+              int dtype, void* stream);
+
+/*
+ * LayerNorm (Emily.Fast docs, section `layer_norm`):
+ *     y[r, j] = (x[r, j] - mean) * rsqrt(var + eps) * w[j] + b[j]
+ * mean and var over the row; var is the population variance (divides by
+ * width).  b may be NULL, which means a zero bias (bitwise the same result).
+ * x, y: [rows, width]; w, b: [width].
+ */
+int fnorm_layer(const void* x, const void* w, const void* b, void* y, int64_t rows,
+                int64_t width, float eps, int dtype, void* stream);
+
+/*
+ * Dual-output query/key head RMSNorm in ONE launch (mlx-c-rust
+ * `compile/norm_fusion.rs`: the query and key head norms that ran as two
+ * launches per layer, produced by one dual-output replay, queries first).
+ *     qy = RMSNorm(q, qw, eps) over head vectors of head_dim
+ *     ky = RMSNorm(k, kw, eps)
+ * q, qy: [q_rows, head_dim] with q_rows = tokens * query heads;
+ * k, ky: [k_rows, head_dim]; qw, kw: [head_dim], shared by all heads.
+ * Results are bitwise equal to fnorm_rms(q, qw, qy, ...) followed by
+ * fnorm_rms(k, kw, ky, ...) with the same eps.  Either row count may be 0
+ * (its pointers may then be NULL).
+ */
+int fnorm_dual_head_rms(const void* q, const void* k, const void* qw, const void* kw, void* qy,
+                        void* ky, int64_t q_rows, int64_t k_rows, int64_t head_dim, float eps,
+                        int dtype, void* stream);
+
+/*
+ * Same calls with an explicit kernel variant: variant -1 is the default
+ * choice (what the calls above use); 0 .. fnorm_variant_count()-1 force one
+ * of the kernels able to serve the request (for testing every instance and
+ * for A/B timing).  Out-of-range variants return FNORM_ERR_UNSUPPORTED.
+ */
+int fnorm_rms_v(const void* x, const void* w, void* y, int64_t rows, int64_t width, float eps,
+                int dtype, void* stream, int variant);
+int fnorm_layer_v(const void* x, const void* w, const void* b, void* y, int64_t rows,
+                  int64_t width, float eps, int dtype, void* stream, int variant);
+int fnorm_dual_head_rms_v(const void* q, const void* k, const void* qw, const void* kw, void* qy,
+                          void* ky, int64_t q_rows, int64_t k_rows, int64_t head_dim, float eps,
+                          int dtype, void* stream, int variant);
+
+/*
+ * Number of kernel variants able to serve (op, dtype, width) when every
+ * pointer is 16-byte aligned (aligned != 0) or not.  Returns 0 for invalid
+ * arguments.  Host-only: makes no HIP call.
+ */
+int fnorm_variant_count(int op, int dtype, int64_t width, int aligned);
+
+/*
+ * Writes into buf (NUL-terminated, at most len bytes) the name of the kernel
+ * and launch shape that variant `variant` (-1 = default) of (op, dtype,
+ * width, aligned) uses, e.g. "rms.bf16.vec8.vpt4.lpr256.blk256.exact.persistent".
+ * Returns FNORM_OK, FNORM_ERR_UNSUPPORTED or FNORM_ERR_NULL.  Host-only.
+ */
+int fnorm_describe(int op, int dtype, int64_t width, int aligned, int variant, char* buf,
+                   int64_t len);
+
+/* Static text of a status code. */
+const char* fnorm_status_string(int status);
+
+/* Text of the last error on the calling thread ("operation: description"),
+ * or "" if the last call succeeded. */
+const char* fnorm_last_error(void);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int fnorm_version(void);
+
+/*
+ * Measurement aid, not a normalization: copies `bytes` bytes from src to dst
+ * with 16-byte loads and stores (the practical HBM ceiling a one-pass norm
+ * is compared with).  bytes must be a multiple of 16 and both pointers
+ * 16-byte aligned, the ranges must not overlap; else FNORM_ERR_SHAPE /
+ * FNORM_ERR_ALIAS.
+ */
+int fnorm_bench_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FNORM_H */

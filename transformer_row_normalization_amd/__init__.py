@@ -1,2 +1,210 @@
-"""transformer_row_normalization_amd: fused last-axis row normalization
-(RMSNorm, LayerNorm, dual-output q/k head RMSNorm) for MI355X (gfx950)."""
+"""transformer_row_normalization_amd: fused last-axis row normalization for
+AMD Instinct MI355X (gfx950).
+
+Thin binding over the C ABI of ``libfnorm.so`` (declared in
+``include/fnorm.h``): it checks shapes, dtypes and devices, passes raw device
+pointers, sizes and the current HIP stream, and raises on a non-zero status.
+Every step of the computation runs in the library's HIP kernels; PyTorch only
+provides device memory and streams.  There is no fallback: if the library is
+missing, every call raises.
+
+  rms_norm(x, w, eps)                    RMSNorm over the last axis
+  layer_norm(x, w, b, eps)               LayerNorm over the last axis (b optional)
+  dual_head_rms_norm(q, k, qw, kw, eps)  q/k head RMSNorm in one launch
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfnorm.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "fnorm.h")
+
+F32, BF16 = 0, 1
+OP_RMS, OP_LAYER, OP_DUAL = 0, 1, 2
+STATUS = {0: "FNORM_OK", 1: "FNORM_ERR_NULL", 2: "FNORM_ERR_SHAPE", 3: "FNORM_ERR_EPS",
+          4: "FNORM_ERR_DTYPE", 5: "FNORM_ERR_ALIAS", 6: "FNORM_ERR_UNSUPPORTED",
+          7: "FNORM_ERR_LAUNCH"}
+
+
+class FnormError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+_SIGNATURES = {
+    "fnorm_rms": ([_P, _P, _P, _I64, _I64, _F, _I, _P], _I),
+    "fnorm_layer": ([_P, _P, _P, _P, _I64, _I64, _F, _I, _P], _I),
+    "fnorm_dual_head_rms": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _F, _I, _P], _I),
+    "fnorm_rms_v": ([_P, _P, _P, _I64, _I64, _F, _I, _P, _I], _I),
+    "fnorm_layer_v": ([_P, _P, _P, _P, _I64, _I64, _F, _I, _P, _I], _I),
+    "fnorm_dual_head_rms_v": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _F, _I, _P, _I], _I),
+    "fnorm_variant_count": ([_I, _I, _I64, _I], _I),
+    "fnorm_describe": ([_I, _I, _I64, _I, _I, ctypes.c_char_p, _I64], _I),
+    "fnorm_status_string": ([_I], ctypes.c_char_p),
+    "fnorm_last_error": ([], ctypes.c_char_p),
+    "fnorm_version": ([], _I),
+    "fnorm_bench_copy": ([_P, _P, _I64, _P], _I),
+}
+
+
+def lib():
+    """The loaded libfnorm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m transformer_row_normalization_amd._build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = l
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/fnorm.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(fnorm_[a-z0-9_]+)\s*\(", text)
+
+
+def _check(status: int):
+    if status != 0:
+        raise FnormError(status, lib().fnorm_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _require(t, name, dtype, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def rms_norm(x, w, eps: float = 1e-6, out=None, variant: int = -1):
+    """y = x * rsqrt(mean(x^2, last axis) + eps) * w  (fp32 or bf16 CUDA tensors)."""
+    torch = _torch()
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    code = _dtype_code(x)
+    _require(x, "x", x.dtype, x.device)
+    width = x.shape[-1] if x.dim() else 1
+    _require(w, "w", x.dtype, x.device)
+    if tuple(w.shape) != (width,):
+        raise ValueError(f"w has shape {tuple(w.shape)}, expected ({width},)")
+    y = torch.empty_like(x) if out is None else out
+    _require(y, "out", x.dtype, x.device)
+    if y.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    rows = x.numel() // width if width else 0
+    _check(lib().fnorm_rms_v(_ptr(x), _ptr(w), _ptr(y), rows, width, eps, code, _stream(x),
+                             variant))
+    return y
+
+
+def layer_norm(x, w, b=None, eps: float = 1e-5, out=None, variant: int = -1):
+    """y = (x - mean) * rsqrt(var + eps) * w + b over the last axis; b may be None."""
+    torch = _torch()
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    code = _dtype_code(x)
+    _require(x, "x", x.dtype, x.device)
+    width = x.shape[-1] if x.dim() else 1
+    _require(w, "w", x.dtype, x.device)
+    if tuple(w.shape) != (width,):
+        raise ValueError(f"w has shape {tuple(w.shape)}, expected ({width},)")
+    if b is not None:
+        _require(b, "b", x.dtype, x.device)
+        if tuple(b.shape) != (width,):
+            raise ValueError(f"b has shape {tuple(b.shape)}, expected ({width},)")
+    y = torch.empty_like(x) if out is None else out
+    _require(y, "out", x.dtype, x.device)
+    if y.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    rows = x.numel() // width if width else 0
+    _check(lib().fnorm_layer_v(_ptr(x), _ptr(w), _ptr(b), _ptr(y), rows, width, eps, code,
+                               _stream(x), variant))
+    return y
+
+
+def dual_head_rms_norm(q, k, qw, kw, eps: float = 1e-6, q_out=None, k_out=None,
+                       variant: int = -1):
+    """One launch: (RMSNorm(q, qw), RMSNorm(k, kw)) over the head dimension
+    (last axis); queries first, keys second."""
+    torch = _torch()
+    if not q.is_cuda:
+        raise ValueError("q must be a GPU tensor")
+    code = _dtype_code(q)
+    hd = q.shape[-1]
+    for t, n in ((q, "q"), (k, "k"), (qw, "qw"), (kw, "kw")):
+        _require(t, n, q.dtype, q.device)
+    if k.shape[-1] != hd or tuple(qw.shape) != (hd,) or tuple(kw.shape) != (hd,):
+        raise ValueError("q, k, qw and kw must share the head dimension")
+    qy = torch.empty_like(q) if q_out is None else q_out
+    ky = torch.empty_like(k) if k_out is None else k_out
+    _require(qy, "q_out", q.dtype, q.device)
+    _require(ky, "k_out", q.dtype, q.device)
+    if qy.shape != q.shape or ky.shape != k.shape:
+        raise ValueError("outputs must match the inputs' shapes")
+    _check(lib().fnorm_dual_head_rms_v(_ptr(q), _ptr(k), _ptr(qw), _ptr(kw), _ptr(qy), _ptr(ky),
+                                       q.numel() // hd, k.numel() // hd, hd, eps, code,
+                                       _stream(q), variant))
+    return qy, ky
+
+
+def variant_count(op: int, dtype_code: int, width: int, aligned: bool = True) -> int:
+    return lib().fnorm_variant_count(op, dtype_code, width, 1 if aligned else 0)
+
+
+def describe(op: int, dtype_code: int, width: int, aligned: bool = True, variant: int = -1) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().fnorm_describe(op, dtype_code, width, 1 if aligned else 0, variant, buf, 256))
+    return buf.value.decode()
+
+
+def bench_copy(src, dst):
+    """16-byte copy kernel over src's bytes (measurement ceiling)."""
+    _check(lib().fnorm_bench_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(),
+                                  _stream(src)))
+    return dst
+
+
+def version() -> int:
+    return lib().fnorm_version()

@@ -1,0 +1,387 @@
+// C ABI of libfnorm: argument validation, kernel selection and launch.
+//
+// Validation runs first and makes no HIP call; only a valid request reaches
+// the device-property queries and the launch.  Errors are reported as a
+// status code plus a per-thread "operation: description" text, the
+// convention of the error type in mlx-c-rust `compile/norm_fusion.rs`
+// (operation name + description, structural checks before any work).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <memory>
+#include <vector>
+
+#include "../../include/fnorm.h"
+#include "fnorm_kernels.hpp"
+#include "fnorm_table.hpp"
+
+namespace fnorm {
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+thread_local char g_err[512];
+
+int fail(int status, const char* op, const char* fmt, ...) {
+    int n = std::snprintf(g_err, sizeof g_err, "%s: ", op);
+    if (n < 0 || n >= int(sizeof g_err)) n = 0;
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err + n, sizeof g_err - n, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return FNORM_OK;
+}
+
+struct Registry {
+    std::vector<Variant> table;
+    std::unique_ptr<std::atomic<int>[]> occupancy;  // blocks per CU, 0 = not yet queried
+};
+
+const Registry& registry() {
+    static const Registry r = [] {
+        Registry reg;
+        register_f32(reg.table);
+        register_bf16(reg.table);
+        reg.occupancy.reset(new std::atomic<int>[reg.table.size()]);
+        for (size_t i = 0; i < reg.table.size(); ++i) reg.occupancy[i].store(0);
+        return reg;
+    }();
+    return r;
+}
+
+int elem_bytes(int dtype) { return dtype == FNORM_F32 ? 4 : 2; }
+const char* dtype_name(int dtype) { return dtype == FNORM_F32 ? "f32" : "bf16"; }
+
+// One runnable choice: a table entry plus the grid policy.
+struct Choice {
+    const Variant* v = nullptr;
+    bool persistent = true;
+};
+
+constexpr int kMaxCandidates = 24;
+
+const Variant* smallest_masked(int kind, int dt, int vec, int64_t width) {
+    const Variant* best = nullptr;
+    for (const Variant& v : registry().table) {
+        if (v.kind != kind || v.dt != dt || v.vec != vec || !v.masked || v.wide) continue;
+        if (v.capacity() < width) continue;
+        if (!best || v.capacity() < best->capacity()) best = &v;
+    }
+    return best;
+}
+
+const Variant* find_wide(int kind, int dt, int vec) {
+    for (const Variant& v : registry().table)
+        if (v.kind == kind && v.dt == dt && v.vec == vec && v.wide) return &v;
+    return nullptr;
+}
+
+// Kernels able to serve (kind, dtype, width, aligned), default first:
+// exact-width resident shapes, then the smallest masked resident shape, then
+// the scalar-access resident shape, then the multi-pass wide kernels.
+int candidates(int kind, int dt, int64_t width, bool aligned, const Variant** out) {
+    int n = 0;
+    const int vec = 16 / elem_bytes(dt);
+    const bool vec_ok = aligned && (width % vec == 0);
+    if (vec_ok) {
+        for (const Variant& v : registry().table)
+            if (v.kind == kind && v.dt == dt && v.vec == vec && !v.masked && !v.wide &&
+                v.capacity() == width && n < kMaxCandidates - 4)
+                out[n++] = &v;
+        if (const Variant* m = smallest_masked(kind, dt, vec, width)) out[n++] = m;
+    }
+    if (const Variant* s = smallest_masked(kind, dt, 1, width)) out[n++] = s;
+    if (kind != K_DUAL) {
+        if (vec_ok)
+            if (const Variant* w = find_wide(kind, dt, vec)) out[n++] = w;
+        if (const Variant* w = find_wide(kind, dt, 1)) out[n++] = w;
+    }
+    return n;
+}
+
+// Variant index i -> candidate i / 2, persistent grid when i is even.
+bool pick(int kind, int dt, int64_t width, bool aligned, int variant, Choice* c) {
+    const Variant* list[kMaxCandidates];
+    const int n = candidates(kind, dt, width, aligned, list);
+    if (variant < 0) variant = 0;
+    if (variant >= 2 * n) return false;
+    c->v = list[variant / 2];
+    c->persistent = (variant % 2) == 0;
+    return true;
+}
+
+int op_kind(int op, bool has_bias) {
+    if (op == FNORM_OP_RMS) return K_RMS;
+    if (op == FNORM_OP_LAYER) return has_bias ? K_LAYER : K_LAYER_NOBIAS;
+    return K_DUAL;
+}
+
+void describe_choice(const Choice& c, char* buf, size_t len) {
+    const Variant& v = *c.v;
+    static const char* kinds[] = {"rms", "layer", "layer", "dual", "copy"};
+    if (v.wide)
+        std::snprintf(buf, len, "%s.%s.vec%d.wide.blk%d.%s", kinds[v.kind], dtype_name(v.dt),
+                      v.vec, v.block, c.persistent ? "persistent" : "grid");
+    else
+        std::snprintf(buf, len, "%s.%s.vec%d.vpt%d.lpr%d.blk%d.%s%s.%s", kinds[v.kind],
+                      dtype_name(v.dt), v.vec, v.vpt, v.lpr, v.block,
+                      v.masked ? "masked" : "exact", v.nt ? ".nt" : "",
+                      c.persistent ? "persistent" : "grid");
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, int64_t an, const void* b, int64_t bn) {
+    if (!a || !b || an <= 0 || bn <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + uintptr_t(bn) && b0 < a0 + uintptr_t(an);
+}
+
+int check_scalars(const char* op, int dtype, int64_t rows, int64_t width, float eps) {
+    if (dtype != FNORM_F32 && dtype != FNORM_BF16)
+        return fail(FNORM_ERR_DTYPE, op, "dtype %d is not FNORM_F32 (0) or FNORM_BF16 (1)", dtype);
+    if (rows < 0 || width <= 0)
+        return fail(FNORM_ERR_SHAPE, op, "rows=%lld width=%lld (need rows >= 0, width > 0)",
+                    (long long)rows, (long long)width);
+    const int64_t limit = INT64_MAX / 8;
+    if (rows > 0 && width > limit / rows)
+        return fail(FNORM_ERR_SHAPE, op, "rows*width overflows (rows=%lld width=%lld)",
+                    (long long)rows, (long long)width);
+    if (!std::isfinite(eps) || eps < 0.0f)
+        return fail(FNORM_ERR_EPS, op, "eps=%g must be finite and >= 0", double(eps));
+    return FNORM_OK;
+}
+
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    std::atomic<int>& slot = cache[dev & 63];
+    int n = slot.load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        slot.store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+int blocks_per_cu(const Variant* v) {
+    const Registry& r = registry();
+    std::atomic<int>& slot = r.occupancy[v - r.table.data()];
+    int n = slot.load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, v->fn, v->block, 0) != hipSuccess ||
+            n <= 0)
+            n = 1;
+        slot.store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+int launch(const char* op, const Choice& c, NormArgs& a, void* stream) {
+    const int64_t rpb = c.v->rows_per_block();
+    const int64_t needed = (a.rows + rpb - 1) / rpb;
+    int64_t grid = needed;
+    if (c.persistent) {
+        const int64_t cap = int64_t(device_cus()) * blocks_per_cu(c.v);
+        if (grid > cap) grid = cap;
+    }
+    if (grid > (int64_t(1) << 30)) grid = int64_t(1) << 30;  // grid-stride covers the rest
+    void* args[] = {&a};
+    hipError_t e = hipLaunchKernel(c.v->fn, dim3(unsigned(grid)), dim3(unsigned(c.v->block)),
+                                   args, 0, static_cast<hipStream_t>(stream));
+    hipError_t e2 = hipGetLastError();
+    if (e == hipSuccess) e = e2;
+    if (e != hipSuccess)
+        return fail(FNORM_ERR_LAUNCH, op, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+}  // namespace fnorm
+
+using namespace fnorm;
+
+extern "C" {
+
+int fnorm_rms_v(const void* x, const void* w, void* y, int64_t rows, int64_t width, float eps,
+                int dtype, void* stream, int variant) {
+    static const char* op = "fnorm_rms";
+    if (int s = check_scalars(op, dtype, rows, width, eps)) return s;
+    if (rows == 0) return ok();
+    if (!x || !w || !y) return fail(FNORM_ERR_NULL, op, "x, w and y must be non-NULL");
+    const int64_t eb = elem_bytes(dtype);
+    const int64_t xb = rows * width * eb;
+    if (y != x && overlap(y, xb, x, xb))
+        return fail(FNORM_ERR_ALIAS, op, "y overlaps x without being equal to it");
+    if (overlap(y, xb, w, width * eb)) return fail(FNORM_ERR_ALIAS, op, "y overlaps w");
+    Choice c;
+    const bool al = aligned16(x) && aligned16(w) && aligned16(y);
+    if (!pick(K_RMS, dtype, width, al, variant, &c))
+        return fail(FNORM_ERR_UNSUPPORTED, op, "no kernel variant %d for width %lld", variant,
+                    (long long)width);
+    NormArgs a{x, w, nullptr, y, nullptr, nullptr, nullptr, rows, rows, width, eps};
+    return launch(op, c, a, stream);
+}
+
+int fnorm_rms(const void* x, const void* w, void* y, int64_t rows, int64_t width, float eps,
+              int dtype, void* stream) {
+    return fnorm_rms_v(x, w, y, rows, width, eps, dtype, stream, -1);
+}
+
+int fnorm_layer_v(const void* x, const void* w, const void* b, void* y, int64_t rows,
+                  int64_t width, float eps, int dtype, void* stream, int variant) {
+    static const char* op = "fnorm_layer";
+    if (int s = check_scalars(op, dtype, rows, width, eps)) return s;
+    if (rows == 0) return ok();
+    if (!x || !w || !y) return fail(FNORM_ERR_NULL, op, "x, w and y must be non-NULL");
+    const int64_t eb = elem_bytes(dtype);
+    const int64_t xb = rows * width * eb;
+    if (y != x && overlap(y, xb, x, xb))
+        return fail(FNORM_ERR_ALIAS, op, "y overlaps x without being equal to it");
+    if (overlap(y, xb, w, width * eb)) return fail(FNORM_ERR_ALIAS, op, "y overlaps w");
+    if (overlap(y, xb, b, width * eb)) return fail(FNORM_ERR_ALIAS, op, "y overlaps b");
+    Choice c;
+    const bool al = aligned16(x) && aligned16(w) && aligned16(y) && (!b || aligned16(b));
+    if (!pick(op_kind(FNORM_OP_LAYER, b != nullptr), dtype, width, al, variant, &c))
+        return fail(FNORM_ERR_UNSUPPORTED, op, "no kernel variant %d for width %lld", variant,
+                    (long long)width);
+    NormArgs a{x, w, b, y, nullptr, nullptr, nullptr, rows, rows, width, eps};
+    return launch(op, c, a, stream);
+}
+
+int fnorm_layer(const void* x, const void* w, const void* b, void* y, int64_t rows,
+                int64_t width, float eps, int dtype, void* stream) {
+    return fnorm_layer_v(x, w, b, y, rows, width, eps, dtype, stream, -1);
+}
+
+int fnorm_dual_head_rms_v(const void* q, const void* k, const void* qw, const void* kw, void* qy,
+                          void* ky, int64_t q_rows, int64_t k_rows, int64_t head_dim, float eps,
+                          int dtype, void* stream, int variant) {
+    static const char* op = "fnorm_dual_head_rms";
+    if (int s = check_scalars(op, dtype, q_rows < k_rows ? q_rows : k_rows, head_dim, eps))
+        return s;
+    if (q_rows > INT64_MAX / 16 - k_rows ||
+        (q_rows + k_rows > 0 && head_dim > (INT64_MAX / 8) / (q_rows + k_rows)))
+        return fail(FNORM_ERR_SHAPE, op, "q_rows + k_rows overflows");
+    if (q_rows + k_rows == 0) return ok();
+    if (q_rows > 0 && (!q || !qw || !qy))
+        return fail(FNORM_ERR_NULL, op, "q, qw and qy must be non-NULL when q_rows > 0");
+    if (k_rows > 0 && (!k || !kw || !ky))
+        return fail(FNORM_ERR_NULL, op, "k, kw and ky must be non-NULL when k_rows > 0");
+    const int64_t eb = elem_bytes(dtype);
+    const int64_t qb = q_rows * head_dim * eb, kb = k_rows * head_dim * eb, wb = head_dim * eb;
+    if (qy != q && overlap(qy, qb, q, qb)) return fail(FNORM_ERR_ALIAS, op, "qy overlaps q");
+    if (ky != k && overlap(ky, kb, k, kb)) return fail(FNORM_ERR_ALIAS, op, "ky overlaps k");
+    if (overlap(qy, qb, k, kb) || overlap(ky, kb, q, qb))
+        return fail(FNORM_ERR_ALIAS, op, "an output overlaps the other tensor's input");
+    if (overlap(qy, qb, ky, kb)) return fail(FNORM_ERR_ALIAS, op, "qy overlaps ky");
+    if (overlap(qy, qb, qw, q_rows > 0 ? wb : 0) || overlap(qy, qb, kw, k_rows > 0 ? wb : 0) ||
+        overlap(ky, kb, qw, q_rows > 0 ? wb : 0) || overlap(ky, kb, kw, k_rows > 0 ? wb : 0))
+        return fail(FNORM_ERR_ALIAS, op, "an output overlaps a weight");
+    const bool al = (q_rows == 0 || (aligned16(q) && aligned16(qw) && aligned16(qy))) &&
+                    (k_rows == 0 || (aligned16(k) && aligned16(kw) && aligned16(ky)));
+    Choice c;
+    if (!pick(K_DUAL, dtype, head_dim, al, variant, &c))
+        return fail(FNORM_ERR_UNSUPPORTED, op, "no kernel variant %d for head_dim %lld", variant,
+                    (long long)head_dim);
+    // A side with no rows is never read; give the kernel the other side's
+    // valid weight pointer so its register preload stays in bounds.
+    const void* qw_eff = q_rows > 0 ? qw : kw;
+    const void* kw_eff = k_rows > 0 ? kw : qw;
+    NormArgs a{q, qw_eff, nullptr, qy, k, kw_eff, ky, q_rows + k_rows, q_rows, head_dim, eps};
+    return launch(op, c, a, stream);
+}
+
+int fnorm_dual_head_rms(const void* q, const void* k, const void* qw, const void* kw, void* qy,
+                        void* ky, int64_t q_rows, int64_t k_rows, int64_t head_dim, float eps,
+                        int dtype, void* stream) {
+    return fnorm_dual_head_rms_v(q, k, qw, kw, qy, ky, q_rows, k_rows, head_dim, eps, dtype,
+                                 stream, -1);
+}
+
+int fnorm_variant_count(int op, int dtype, int64_t width, int aligned) {
+    if ((dtype != FNORM_F32 && dtype != FNORM_BF16) || width <= 0 || op < 0 || op > 2) return 0;
+    const Variant* list[kMaxCandidates];
+    return 2 * candidates(op_kind(op, true), dtype, width, aligned != 0, list);
+}
+
+int fnorm_describe(int op, int dtype, int64_t width, int aligned, int variant, char* buf,
+                   int64_t len) {
+    static const char* name = "fnorm_describe";
+    if (!buf || len <= 0) return fail(FNORM_ERR_NULL, name, "buf must be non-NULL, len > 0");
+    buf[0] = '\0';
+    if (dtype != FNORM_F32 && dtype != FNORM_BF16)
+        return fail(FNORM_ERR_DTYPE, name, "dtype %d", dtype);
+    if (width <= 0) return fail(FNORM_ERR_SHAPE, name, "width %lld", (long long)width);
+    if (op < 0 || op > 2) return fail(FNORM_ERR_UNSUPPORTED, name, "op %d", op);
+    Choice c;
+    if (!pick(op_kind(op, true), dtype, width, aligned != 0, variant, &c))
+        return fail(FNORM_ERR_UNSUPPORTED, name, "no variant %d", variant);
+    describe_choice(c, buf, size_t(len));
+    return ok();
+}
+
+const char* fnorm_status_string(int status) {
+    switch (status) {
+        case FNORM_OK: return "FNORM_OK";
+        case FNORM_ERR_NULL: return "FNORM_ERR_NULL: required pointer is NULL";
+        case FNORM_ERR_SHAPE: return "FNORM_ERR_SHAPE: invalid rows/width";
+        case FNORM_ERR_EPS: return "FNORM_ERR_EPS: eps must be finite and >= 0";
+        case FNORM_ERR_DTYPE: return "FNORM_ERR_DTYPE: unknown dtype";
+        case FNORM_ERR_ALIAS: return "FNORM_ERR_ALIAS: output overlaps another buffer";
+        case FNORM_ERR_UNSUPPORTED: return "FNORM_ERR_UNSUPPORTED: no kernel for this request";
+        case FNORM_ERR_LAUNCH: return "FNORM_ERR_LAUNCH: HIP launch failed";
+        default: return "unknown fnorm status";
+    }
+}
+
+const char* fnorm_last_error(void) { return g_err; }
+
+int fnorm_version(void) { return kVersion; }
+
+int fnorm_bench_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    static const char* op = "fnorm_bench_copy";
+    if (!src || !dst) return fail(FNORM_ERR_NULL, op, "src and dst must be non-NULL");
+    if (bytes < 0 || bytes % 16 != 0 || !aligned16(src) || !aligned16(dst))
+        return fail(FNORM_ERR_SHAPE, op, "bytes must be a multiple of 16, pointers 16-B aligned");
+    if (overlap(src, bytes, dst, bytes)) return fail(FNORM_ERR_ALIAS, op, "src overlaps dst");
+    if (bytes == 0) return ok();
+    constexpr int kBlock = 256;
+    const void* fn = reinterpret_cast<const void*>(&copy16<kBlock>);
+    static std::atomic<int> occ{0};
+    int per_cu = occ.load(std::memory_order_relaxed);
+    if (per_cu <= 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlock, 0) != hipSuccess ||
+            per_cu <= 0)
+            per_cu = 1;
+        occ.store(per_cu, std::memory_order_relaxed);
+    }
+    const int64_t n16 = bytes / 16;
+    int64_t grid = (n16 + kBlock - 1) / kBlock;
+    const int64_t cap = int64_t(device_cus()) * per_cu;
+    if (grid > cap) grid = cap;
+    const u32x4* s = static_cast<const u32x4*>(src);
+    u32x4* d = static_cast<u32x4*>(dst);
+    int64_t n = n16;
+    void* args[] = {&s, &d, &n};
+    hipError_t e = hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(kBlock), args, 0,
+                                   static_cast<hipStream_t>(stream));
+    hipError_t e2 = hipGetLastError();
+    if (e == hipSuccess) e = e2;
+    if (e != hipSuccess) return fail(FNORM_ERR_LAUNCH, op, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,189 @@
+// Device-side building blocks of the row-normalization kernels (gfx950).
+//
+//  * Raw element packs: 16-byte vectors (4 x fp32 or 8 x bf16) for the
+//    coalesced path, single elements for the scalar path.  Rows stay in
+//    registers as raw bits and are widened to fp32 at each use.
+//  * bf16 <-> fp32: widening is a shift (bf16 is the high half of a
+//    binary32); narrowing is round-to-nearest-even via gfx950's packed
+//    v_cvt_pk_bf16_f32.
+//  * Cross-lane sums with a fixed butterfly: after each step every lane of
+//    the group holds the same bits (a + b computed in both lanes of a pair
+//    is the same IEEE result), so row scalars are identical in every lane
+//    and the reduction order depends only on the launch shape.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fnorm {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1 };
+enum : int { OP_RMS = 0, OP_LAYER = 1 };
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- packs
+template <int DT, int VEC> struct Raw;
+template <> struct Raw<DT_F32, 4> { using type = u32x4; };
+template <> struct Raw<DT_BF16, 8> { using type = u32x4; };
+template <> struct Raw<DT_F32, 1> { using type = uint32_t; };
+template <> struct Raw<DT_BF16, 1> { using type = uint16_t; };
+
+template <int DT> struct Elem;
+template <> struct Elem<DT_F32> { static constexpr int bytes = 4; };
+template <> struct Elem<DT_BF16> { static constexpr int bytes = 2; };
+
+template <int DT, int VEC>
+__device__ __forceinline__ typename Raw<DT, VEC>::type raw_zero() {
+    return typename Raw<DT, VEC>::type(0);
+}
+
+// Load the pack that starts at element `idx` of `base`.  NT selects the
+// non-temporal (streaming) cache policy.
+template <int DT, int VEC, bool NT>
+__device__ __forceinline__ typename Raw<DT, VEC>::type load_raw(const void* base, int64_t idx) {
+    using R = typename Raw<DT, VEC>::type;
+    const R* p = reinterpret_cast<const R*>(static_cast<const char*>(base) +
+                                            idx * Elem<DT>::bytes);
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <int DT, int VEC, bool NT>
+__device__ __forceinline__ void store_raw(void* base, int64_t idx, typename Raw<DT, VEC>::type v) {
+    using R = typename Raw<DT, VEC>::type;
+    R* p = reinterpret_cast<R*>(static_cast<char*>(base) + idx * Elem<DT>::bytes);
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
+
+// Element i of a pack, widened to fp32 (exact).
+template <int DT, int VEC>
+__device__ __forceinline__ float elem(const typename Raw<DT, VEC>::type& r, int i) {
+    if constexpr (VEC == 1) {
+        if constexpr (DT == DT_F32) return __builtin_bit_cast(float, r);
+        else return __builtin_bit_cast(float, uint32_t(r) << 16);
+    } else if constexpr (DT == DT_F32) {
+        // Copy the component out first: bit_cast of a vector-component
+        // lvalue reads component 0 whatever the index.
+        const uint32_t u = r[i];
+        return __builtin_bit_cast(float, u);
+    } else {
+        return (i & 1) ? bf16_hi(r[i >> 1]) : bf16_lo(r[i >> 1]);
+    }
+}
+
+// Two fp32 values rounded to bf16 (nearest, ties to even), packed lo | hi << 16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 h = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// VEC fp32 values stored into a pack of the element type.
+template <int DT, int VEC>
+__device__ __forceinline__ typename Raw<DT, VEC>::type make_raw(const float (&f)[VEC]) {
+    if constexpr (VEC == 1) {
+        if constexpr (DT == DT_F32) return __builtin_bit_cast(uint32_t, f[0]);
+        else return uint16_t(pack_bf16x2(f[0], 0.0f) & 0xFFFFu);
+    } else if constexpr (DT == DT_F32) {
+        return u32x4{__builtin_bit_cast(uint32_t, f[0]), __builtin_bit_cast(uint32_t, f[1]),
+                     __builtin_bit_cast(uint32_t, f[2]), __builtin_bit_cast(uint32_t, f[3])};
+    } else {
+        return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                     pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+    }
+}
+
+// ---------------------------------------------------------------- reductions
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// DPP controls (GFX9 encoding): quad permutes, and the in-row mirrors.
+constexpr int DPP_QUAD_1032 = 0xB1;      // lane ^ 1
+constexpr int DPP_QUAD_2301 = 0x4E;      // lane ^ 2
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <- lane 7 - i within 8
+constexpr int DPP_ROW_MIRROR = 0x140;       // lane i <- lane 15 - i within 16
+constexpr int SWIZZLE_XOR16 = 0x401F;       // bitmask mode: and 0x1f, xor 0x10
+
+// Sum over aligned groups of G consecutive lanes (G a power of two <= 64).
+// Each step adds a value that is already uniform over the partner half, so
+// the result is bitwise identical in every lane of the group.
+template <int G>
+__device__ __forceinline__ float lane_group_sum(float v) {
+    static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "group size");
+    if constexpr (G >= 2) v += dpp<DPP_QUAD_1032>(v);
+    if constexpr (G >= 4) v += dpp<DPP_QUAD_2301>(v);
+    if constexpr (G >= 8) v += dpp<DPP_ROW_HALF_MIRROR>(v);
+    if constexpr (G >= 16) v += dpp<DPP_ROW_MIRROR>(v);
+    if constexpr (G >= 32)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                                   SWIZZLE_XOR16));
+    if constexpr (G >= 64) {
+        const int lane = __lane_id();
+        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2,
+                                                                    __builtin_bit_cast(int, v)));
+    }
+    return v;
+}
+
+// Sum over a group of LPR threads that owns one row.  LPR <= 64: lanes of one
+// wavefront.  LPR > 64: LPR/64 whole wavefronts; each wave reduces, writes
+// one partial to LDS, one barrier, then every thread adds the partials of
+// its row in wave order.  `lds` has RPB * (LPR/64) slots for this call site;
+// the caller keeps call sites apart so that a slot is never rewritten while
+// a slower wave may still read it.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v, float* lds, int group, int lane_in_row) {
+    if constexpr (LPR <= 64) {
+        return lane_group_sum<LPR>(v);
+    } else {
+        constexpr int WPR = LPR / 64;
+        v = lane_group_sum<64>(v);
+        const int wave = lane_in_row >> 6;
+        if ((lane_in_row & 63) == 0) lds[group * WPR + wave] = v;
+        __syncthreads();
+        float s = lds[group * WPR];
+#pragma unroll
+        for (int i = 1; i < WPR; ++i) s += lds[group * WPR + i];
+        return s;
+    }
+}
+
+// Two sums over the same row group at once (one barrier for both): `a` in
+// slots lds_a, `b` in slots lds_b, each laid out like row_sum's.
+template <int LPR>
+__device__ __forceinline__ void row_sum2(float& a, float& b, float* lds_a, float* lds_b, int group,
+                                         int lane_in_row) {
+    if constexpr (LPR <= 64) {
+        a = lane_group_sum<LPR>(a);
+        b = lane_group_sum<LPR>(b);
+    } else {
+        constexpr int WPR = LPR / 64;
+        a = lane_group_sum<64>(a);
+        b = lane_group_sum<64>(b);
+        const int wave = lane_in_row >> 6;
+        if ((lane_in_row & 63) == 0) {
+            lds_a[group * WPR + wave] = a;
+            lds_b[group * WPR + wave] = b;
+        }
+        __syncthreads();
+        float sa = lds_a[group * WPR], sb = lds_b[group * WPR];
+#pragma unroll
+        for (int i = 1; i < WPR; ++i) {
+            sa += lds_a[group * WPR + i];
+            sb += lds_b[group * WPR + i];
+        }
+        a = sa;
+        b = sb;
+    }
+}
+
+}  // namespace fnorm

@@ -1,0 +1,122 @@
+// Instantiation list shared by the two per-dtype translation units.
+//
+// Shapes are (VPT, LPR, BLOCK) for the 16-byte pack width of the element
+// type (fp32x4 / bf16x8).  "exact" shapes have capacity lpr*vpt*vec equal to
+// the width they serve and carry no column predicate; "masked" shapes serve
+// every smaller width too.  Within one capacity the first registered shape
+// is the default, so the order below is the preference order.
+#pragma once
+
+#include "fnorm_kernels.hpp"
+#include "fnorm_table.hpp"
+
+namespace fnorm {
+
+template <int KIND, int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, bool NT>
+inline Variant make_variant() {
+    constexpr int OP = (KIND == K_LAYER || KIND == K_LAYER_NOBIAS) ? OP_LAYER : OP_RMS;
+    constexpr bool BIAS = KIND == K_LAYER;
+    constexpr bool DUAL = KIND == K_DUAL;
+    Variant v{};
+    v.fn = reinterpret_cast<const void*>(
+        &norm_rows<OP, DT, VEC, VPT, LPR, BLOCK, MASKED, BIAS, DUAL, NT>);
+    v.kind = KIND;
+    v.dt = DT;
+    v.vec = VEC;
+    v.vpt = VPT;
+    v.lpr = LPR;
+    v.block = BLOCK;
+    v.masked = MASKED;
+    v.nt = NT;
+    v.wide = false;
+    return v;
+}
+
+template <int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, bool NT>
+inline void add_shape(std::vector<Variant>& t) {
+    t.push_back(make_variant<K_RMS, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>());
+    t.push_back(make_variant<K_LAYER, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>());
+    t.push_back(make_variant<K_LAYER_NOBIAS, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>());
+    t.push_back(make_variant<K_DUAL, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>());
+}
+
+template <int KIND, int DT, int VEC, int BLOCK>
+inline Variant make_wide() {
+    constexpr int OP = (KIND == K_LAYER || KIND == K_LAYER_NOBIAS) ? OP_LAYER : OP_RMS;
+    Variant v{};
+    v.fn = reinterpret_cast<const void*>(&norm_rows_wide<OP, DT, VEC, BLOCK, KIND == K_LAYER>);
+    v.kind = KIND;
+    v.dt = DT;
+    v.vec = VEC;
+    v.vpt = 0;
+    v.lpr = BLOCK;
+    v.block = BLOCK;
+    v.masked = true;
+    v.nt = false;
+    v.wide = true;
+    return v;
+}
+
+template <int DT, int VEC>
+inline void add_wide(std::vector<Variant>& t) {
+    t.push_back(make_wide<K_RMS, DT, VEC, 1024>());
+    t.push_back(make_wide<K_LAYER, DT, VEC, 1024>());
+    t.push_back(make_wide<K_LAYER_NOBIAS, DT, VEC, 1024>());
+}
+
+// Masked shapes for any width up to 8192 packs, used with pack width V
+// (16-byte packs) and with V = 1 (scalar path for misaligned data or widths
+// that are not a multiple of the pack).
+template <int DT, int V>
+inline void add_masked(std::vector<Variant>& t) {
+    add_shape<DT, V, 1, 1, 256, true, false>(t);
+    add_shape<DT, V, 1, 2, 256, true, false>(t);
+    add_shape<DT, V, 1, 4, 256, true, false>(t);
+    add_shape<DT, V, 1, 8, 256, true, false>(t);
+    add_shape<DT, V, 1, 16, 256, true, false>(t);
+    add_shape<DT, V, 1, 32, 256, true, false>(t);
+    add_shape<DT, V, 1, 64, 256, true, false>(t);
+    add_shape<DT, V, 2, 64, 256, true, false>(t);
+    add_shape<DT, V, 4, 64, 256, true, false>(t);
+    add_shape<DT, V, 8, 64, 256, true, false>(t);
+    add_shape<DT, V, 4, 256, 256, true, false>(t);
+    add_shape<DT, V, 8, 256, 256, true, false>(t);
+    add_shape<DT, V, 4, 1024, 1024, true, false>(t);
+    add_shape<DT, V, 8, 1024, 1024, true, false>(t);
+}
+
+#define FNORM_EXACT(DT, V, VPT, LPR, BLOCK)                \
+    add_shape<DT, V, VPT, LPR, BLOCK, false, false>(t);    \
+    add_shape<DT, V, VPT, LPR, BLOCK, false, true>(t);
+
+template <int DT>
+inline void register_dtype(std::vector<Variant>& t) {
+    constexpr int V = 16 / Elem<DT>::bytes;
+    // exact shapes, preference order within a capacity
+    FNORM_EXACT(DT, V, 1, 16, 256)      // 16 packs (bf16 128 / f32 64)
+    FNORM_EXACT(DT, V, 2, 16, 256)      // 32 packs
+    FNORM_EXACT(DT, V, 1, 32, 256)
+    FNORM_EXACT(DT, V, 3, 32, 256)      // 96 packs (bf16 768)
+    FNORM_EXACT(DT, V, 1, 64, 256)      // 64 packs
+    FNORM_EXACT(DT, V, 2, 64, 256)      // 128 packs (bf16 1024)
+    FNORM_EXACT(DT, V, 3, 64, 256)      // 192 packs (f32 768)
+    FNORM_EXACT(DT, V, 4, 64, 256)      // 256 packs (f32 1024, bf16 2048)
+    FNORM_EXACT(DT, V, 1, 256, 256)
+    FNORM_EXACT(DT, V, 8, 64, 256)      // 512 packs (bf16 4096)
+    FNORM_EXACT(DT, V, 2, 256, 256)
+    FNORM_EXACT(DT, V, 1, 512, 512)
+    FNORM_EXACT(DT, V, 4, 256, 256)     // 1024 packs (bf16 8192, f32 4096)
+    FNORM_EXACT(DT, V, 2, 512, 512)
+    FNORM_EXACT(DT, V, 1, 1024, 1024)
+    FNORM_EXACT(DT, V, 8, 256, 256)     // 2048 packs (f32 8192)
+    FNORM_EXACT(DT, V, 4, 512, 512)
+    FNORM_EXACT(DT, V, 2, 1024, 1024)
+    add_masked<DT, V>(t);
+    add_masked<DT, 1>(t);
+    add_wide<DT, V>(t);
+    add_wide<DT, 1>(t);
+}
+
+#undef FNORM_EXACT
+
+}  // namespace fnorm

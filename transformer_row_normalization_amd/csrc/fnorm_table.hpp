@@ -1,0 +1,38 @@
+// The dispatch table: one entry per compiled kernel instance.
+//
+// An entry records the launch shape of a `norm_rows` / `norm_rows_wide`
+// instance (element type, pack width VEC, packs per thread VPT, threads per
+// row LPR, threads per block) and which operation kind it serves.  The host
+// side (fnorm_api.hip) turns (op, dtype, width, alignment) into an ordered
+// list of entries able to run it; the first is the default.
+#pragma once
+
+#include <stdint.h>
+
+#include <vector>
+
+namespace fnorm {
+
+enum Kind : int { K_RMS = 0, K_LAYER = 1, K_LAYER_NOBIAS = 2, K_DUAL = 3, K_COPY = 4 };
+
+struct Variant {
+    const void* fn;     // host stub of the __global__ function
+    int kind;           // Kind
+    int dt;             // DT_F32 / DT_BF16
+    int vec;            // elements per access
+    int vpt;            // packs per thread (resident kernels)
+    int lpr;            // threads per row
+    int block;          // threads per workgroup
+    bool masked;        // handles width < lpr*vpt*vec (per-pack predicate)
+    bool nt;            // non-temporal loads/stores of x and y
+    bool wide;          // non-resident multi-pass kernel
+    int64_t capacity() const { return wide ? INT64_MAX : int64_t(lpr) * vpt * vec; }
+    int rows_per_block() const { return wide ? 1 : block / lpr; }
+};
+
+// Defined in fnorm_inst_f32.hip / fnorm_inst_bf16.hip: append every
+// instance of that element type, in preference order.
+void register_f32(std::vector<Variant>& table);
+void register_bf16(std::vector<Variant>& table);
+
+}  // namespace fnorm
