@@ -9,15 +9,16 @@ input, inputs resident in HBM:
 
 Metric: achieved HBM GB/s over the algorithmic bytes (read x once, write y
 once, read the weights/bias once per launch) and rows/s.  Timing: W warm-up
-steps, then K steps bracketed by synchronize, HIP events recorded on the
+steps (default 200, about 60 ms: per-kernel times drift down for the first
+tens of ms of sustained load), then K steps bracketed by synchronize, HIP events recorded on the
 stream the kernels run on around every launch (per-kernel durations) and
 around the whole region.  The step order makes every input cold in the
 caches: 1.6 GB of other traffic separates two reads of the same tensor, more
 than the 256 MB MALL.
 
-Prints ONE JSON line.  Extra legs (outside the timed region): the 16-byte
+Prints ONE JSON line.  Extra legs (outside the timed region): the plain
 copy kernel over the LayerNorm's bytes (practical ceiling) and the fp64 CPU
-oracle over one step's rows (``cpu_baseline``).
+oracle over full steps for about 10 s (``cpu_baseline``).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -49,8 +50,10 @@ def kernel_source_hash() -> str:
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=200,
+                   help="untimed steps; the GPU needs tens of ms of sustained load "
+                        "before its clocks settle")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--ops", default="dual,rms,layer", help="subset of the step, for profiling")
     return p.parse_args()
@@ -212,28 +215,35 @@ def cpu_baseline(wl_dual, wl_rms, wl_ln, log):
     from tests import helpers
 
     o = oracle.default()
-    log("[bench] cpu baseline (oracle, 1 thread, one full step)")
+    log("[bench] cpu baseline (oracle, 1 thread, full steps for >= 10 s)")
     t = wl_dual.tensors
     arr = {k: helpers.to_oracle_array(t[k]) for k in ("q", "k", "qw", "kw")}
-    total_bytes = 0
-    t0 = time.perf_counter()
-    o.dual_head_rms(arr["q"], arr["k"], arr["qw"], arr["kw"], wl_dual.eps)
-    total_bytes += sum(v.nbytes for v in arr.values()) + arr["q"].nbytes + arr["k"].nbytes
+    big = []
     for wl, op in ((wl_rms, "rms"), (wl_ln, "layer")):
-        x = helpers.to_oracle_array(wl.tensors["x"])
-        w = helpers.to_oracle_array(wl.tensors["w"])
         b = helpers.to_oracle_array(wl.tensors["b"]) if "b" in wl.tensors else None
-        for r0 in range(0, x.shape[0], 2048):
-            if op == "rms":
-                o.rms(x[r0:r0 + 2048], w, wl.eps)
-            else:
-                o.layer(x[r0:r0 + 2048], w, b, wl.eps)
-        total_bytes += 2 * x.nbytes + w.nbytes + (b.nbytes if b is not None else 0)
+        big.append((op, helpers.to_oracle_array(wl.tensors["x"]),
+                    helpers.to_oracle_array(wl.tensors["w"]), b, wl.eps))
+    step_bytes = sum(v.nbytes for v in arr.values()) + arr["q"].nbytes + arr["k"].nbytes
+    step_bytes += sum(2 * x.nbytes + w.nbytes + (b.nbytes if b is not None else 0)
+                      for _, x, w, b, _ in big)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        o.dual_head_rms(arr["q"], arr["k"], arr["qw"], arr["kw"], wl_dual.eps)
+        for op, x, w, b, eps in big:
+            for r0 in range(0, x.shape[0], 2048):
+                if op == "rms":
+                    o.rms(x[r0:r0 + 2048], w, eps)
+                else:
+                    o.layer(x[r0:r0 + 2048], w, b, eps)
+        steps += 1
+        if time.perf_counter() - t0 >= 10.0:
+            break
     dt = time.perf_counter() - t0
-    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": "one full step (all rows of the three workloads), fp64 C oracle, "
-                      "single thread, outputs in 2048-row chunks",
+    return {"value": round(steps * step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(dt, 3), "steps": steps,
+            "sample": f"{steps} full steps (all rows of the three workloads) through the fp64 C "
+                      "oracle, single thread, outputs in 2048-row chunks; same algorithmic bytes",
             "host_cpus": os.cpu_count()}
 
 

@@ -77,8 +77,10 @@ int fnorm_layer(const void* x, const void* w, const void* b, void* y, int64_t ro
 
 /*
  * Dual-output query/key head RMSNorm in ONE launch (mlx-c-rust
- * `compile/norm_fusion.rs`: the query and key head norms that ran as two
- * launches per layer, produced by one dual-output replay, queries first).
+ * `compile/norm_fusion.rs`, module docs and the dual head-norm graph
+ * builder: the per-head RMSNorms of queries and of keys, each with its own
+ * scale weight and one shared eps, fused so a layer issues one launch for
+ * both; the normalized queries are the first output, the keys the second).
  *     qy = RMSNorm(q, qw, eps) over head vectors of head_dim
  *     ky = RMSNorm(k, kw, eps)
  * q, qy: [q_rows, head_dim] with q_rows = tokens * query heads;

@@ -131,6 +131,10 @@ void describe_choice(const Choice& c, char* buf, size_t len) {
     if (v.wide)
         std::snprintf(buf, len, "%s.%s.vec%d.wide.blk%d.%s", kinds[v.kind], dtype_name(v.dt),
                       v.vec, v.block, c.persistent ? "persistent" : "grid");
+    else if (c.persistent && v.grid_cap > 0)
+        std::snprintf(buf, len, "%s.%s.vec%d.vpt%d.lpr%d.blk%d.%s%s.persistent%d", kinds[v.kind],
+                      dtype_name(v.dt), v.vec, v.vpt, v.lpr, v.block,
+                      v.masked ? "masked" : "exact", v.nt ? ".nt" : "", v.grid_cap);
     else
         std::snprintf(buf, len, "%s.%s.vec%d.vpt%d.lpr%d.blk%d.%s%s.%s", kinds[v.kind],
                       dtype_name(v.dt), v.vec, v.vpt, v.lpr, v.block,
@@ -194,7 +198,9 @@ int launch(const char* op, const Choice& c, NormArgs& a, void* stream) {
     const int64_t needed = (a.rows + rpb - 1) / rpb;
     int64_t grid = needed;
     if (c.persistent) {
-        const int64_t cap = int64_t(device_cus()) * blocks_per_cu(c.v);
+        int per_cu = blocks_per_cu(c.v);
+        if (c.v->grid_cap > 0 && c.v->grid_cap < per_cu) per_cu = c.v->grid_cap;
+        const int64_t cap = int64_t(device_cus()) * per_cu;
         if (grid > cap) grid = cap;
     }
     if (grid > (int64_t(1) << 30)) grid = int64_t(1) << 30;  // grid-stride covers the rest
@@ -358,20 +364,13 @@ int fnorm_bench_copy(const void* src, void* dst, int64_t bytes, void* stream) {
         return fail(FNORM_ERR_SHAPE, op, "bytes must be a multiple of 16, pointers 16-B aligned");
     if (overlap(src, bytes, dst, bytes)) return fail(FNORM_ERR_ALIAS, op, "src overlaps dst");
     if (bytes == 0) return ok();
-    constexpr int kBlock = 256;
-    const void* fn = reinterpret_cast<const void*>(&copy16<kBlock>);
-    static std::atomic<int> occ{0};
-    int per_cu = occ.load(std::memory_order_relaxed);
-    if (per_cu <= 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlock, 0) != hipSuccess ||
-            per_cu <= 0)
-            per_cu = 1;
-        occ.store(per_cu, std::memory_order_relaxed);
-    }
+    // Full grid, 4 packs per thread: the best plain-copy shape measured on
+    // MI355X.
+    constexpr int kBlock = 256, kU = 4;
+    const void* fn = reinterpret_cast<const void*>(&copy16<kBlock, kU>);
     const int64_t n16 = bytes / 16;
-    int64_t grid = (n16 + kBlock - 1) / kBlock;
-    const int64_t cap = int64_t(device_cus()) * per_cu;
-    if (grid > cap) grid = cap;
+    int64_t grid = (n16 + kBlock * kU - 1) / (kBlock * kU);
+    if (grid > (int64_t(1) << 30)) grid = int64_t(1) << 30;
     const u32x4* s = static_cast<const u32x4*>(src);
     u32x4* d = static_cast<u32x4*>(dst);
     int64_t n = n16;

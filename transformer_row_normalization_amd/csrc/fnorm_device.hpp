@@ -99,6 +99,16 @@ __device__ __forceinline__ typename Raw<DT, VEC>::type make_raw(const float (&f)
     }
 }
 
+// Register-pressure control: an empty asm that "modifies" the packs makes
+// their widened fp32 values non-invariant, so the compiler re-widens them at
+// each use (one VALU op per element) instead of hoisting VPT*VEC fp32 copies
+// out of the row loop and holding them in VGPRs for the whole kernel.
+template <int N, typename R>
+__device__ __forceinline__ void keep_packed(R (&p)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(p[i]));
+}
+
 // ---------------------------------------------------------------- reductions
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {

@@ -56,35 +56,50 @@ template <int OP, int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, boo
           bool DUAL, bool NT>
 __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
     using R = typename Raw<DT, VEC>::type;
-    static_assert(BLOCK % 64 == 0 && (LPR <= 64 ? BLOCK % LPR == 0 : BLOCK % LPR == 0), "shape");
+    static_assert(BLOCK % 64 == 0 && BLOCK % LPR == 0, "launch shape");
     constexpr int RPB = BLOCK / LPR;                 // rows per block-row
     constexpr int WPR = LPR > 64 ? LPR / 64 : 1;     // waves per row
     constexpr int LDS_SLOTS = LPR > 64 ? RPB * WPR : 1;
     __shared__ float red[3][LDS_SLOTS];
+    // Registers vs VALU work: with few elements per thread, let the compiler
+    // keep the widened fp32 copies of x (across the passes) and of the
+    // weights (across rows), saving a widening op per element per use; with
+    // many, keep them as raw packs so the VGPR count (and so occupancy)
+    // stays bounded.
+    constexpr int E = VPT * VEC;
+    constexpr bool PACK_X = E > 32;
+    constexpr bool PACK_W = E > 16;
 
     const int tid = threadIdx.x;
     const int group = tid / LPR;
     const int lane = tid % LPR;
     const int64_t width = a.width;
     const float fwidth = static_cast<float>(width);
+    const int64_t last = a.rows - 1;
+
+    // Column of pack v of this thread, and whether it lies inside the row.
+    auto col_of = [&](int v) { return int64_t(v * LPR + lane) * VEC; };
+    auto in_row = [&](int v) { return !MASKED || col_of(v) < width; };
 
     R wv[VPT];
     R bv[BIAS ? VPT : 1];
     R wv2[DUAL ? VPT : 1];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
-        const int64_t col = int64_t(v * LPR + lane) * VEC;
-        const bool ok = !MASKED || col < width;
-        wv[v] = ok ? load_raw<DT, VEC, false>(a.w, col) : raw_zero<DT, VEC>();
-        if constexpr (BIAS) bv[v] = ok ? load_raw<DT, VEC, false>(a.b, col) : raw_zero<DT, VEC>();
-        if constexpr (DUAL) wv2[v] = ok ? load_raw<DT, VEC, false>(a.w2, col) : raw_zero<DT, VEC>();
+        wv[v] = in_row(v) ? load_raw<DT, VEC, false>(a.w, col_of(v)) : raw_zero<DT, VEC>();
+        if constexpr (BIAS)
+            bv[v] = in_row(v) ? load_raw<DT, VEC, false>(a.b, col_of(v)) : raw_zero<DT, VEC>();
+        if constexpr (DUAL)
+            wv2[v] = in_row(v) ? load_raw<DT, VEC, false>(a.w2, col_of(v)) : raw_zero<DT, VEC>();
     }
 
     int parity = 0;
     for (int64_t base = int64_t(blockIdx.x) * RPB; base < a.rows;
          base += int64_t(gridDim.x) * RPB) {
-        const int64_t row = base + group;
-        const bool valid = row < a.rows;
+        // Row groups past the end re-read the last row (in bounds, so the
+        // loads need no predicate) and store nothing.
+        const bool valid = base + group <= last;
+        const int64_t row = valid ? base + group : last;
         const void* xp = a.x;
         void* yp = a.y;
         int64_t r = row;
@@ -98,16 +113,20 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
             }
         }
         const int64_t row_off = r * width;
+        if constexpr (PACK_W) {
+            keep_packed<VPT>(wv);
+            if constexpr (BIAS) keep_packed<VPT>(bv);
+            if constexpr (DUAL) keep_packed<VPT>(wv2);
+        }
 
         R xv[VPT];
 #pragma unroll
-        for (int v = 0; v < VPT; ++v) {
-            const int64_t col = int64_t(v * LPR + lane) * VEC;
-            const bool ok = valid && (!MASKED || col < width);
-            xv[v] = ok ? load_raw<DT, VEC, NT>(xp, row_off + col) : raw_zero<DT, VEC>();
-        }
+        for (int v = 0; v < VPT; ++v)
+            xv[v] = in_row(v) ? load_raw<DT, VEC, NT>(xp, row_off + col_of(v))
+                              : raw_zero<DT, VEC>();
 
-        float out[VPT][VEC];
+        // Row scalars: out = (x - shift) * scale * w + bias.
+        float shift = 0.0f, scale;
         if constexpr (OP == OP_RMS) {
             float ss = 0.0f;
 #pragma unroll
@@ -119,15 +138,8 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
                 }
             ss = row_sum<LPR>(ss, red[parity], group, lane);
             parity ^= 1;
-            const float s = __builtin_amdgcn_rsqf(ss / fwidth + a.eps);
-#pragma unroll
-            for (int v = 0; v < VPT; ++v) {
-                R wr = wv[v];
-                if constexpr (DUAL) wr = second ? wv2[v] : wv[v];
-#pragma unroll
-                for (int i = 0; i < VEC; ++i)
-                    out[v][i] = (elem<DT, VEC>(xv[v], i) * s) * elem<DT, VEC>(wr, i);
-            }
+            scale = __builtin_amdgcn_rsqf(ss / fwidth + a.eps);
+            if constexpr (PACK_X) keep_packed<VPT>(xv);
         } else {
             float sum = 0.0f;
 #pragma unroll
@@ -136,11 +148,11 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
                 for (int i = 0; i < VEC; ++i) sum += elem<DT, VEC>(xv[v], i);
             sum = row_sum<LPR>(sum, red[0], group, lane);
             const float mean = sum / fwidth;
+            if constexpr (PACK_X) keep_packed<VPT>(xv);
             float sd = 0.0f, sq = 0.0f;
 #pragma unroll
             for (int v = 0; v < VPT; ++v) {
-                const int64_t col = int64_t(v * LPR + lane) * VEC;
-                if (!MASKED || col < width) {
+                if (in_row(v)) {
 #pragma unroll
                     for (int i = 0; i < VEC; ++i) {
                         const float d = elem<DT, VEC>(xv[v], i) - mean;
@@ -152,22 +164,36 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
             row_sum2<LPR>(sd, sq, red[1], red[2], group, lane);
             const float c = sd / fwidth;
             const float var = __builtin_fmaxf((sq - c * sd) / fwidth, 0.0f);
-            const float s = __builtin_amdgcn_rsqf(var + a.eps);
+            scale = __builtin_amdgcn_rsqf(var + a.eps);
+            shift = mean;
+            if constexpr (PACK_X) keep_packed<VPT>(xv);
+            // x - mean - c is evaluated as (x - mean) - c below.
+            if (valid) {
 #pragma unroll
-            for (int v = 0; v < VPT; ++v)
+                for (int v = 0; v < VPT; ++v) {
+                    float o[VEC];
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) {
-                    const float d = (elem<DT, VEC>(xv[v], i) - mean) - c;
-                    const float bias = BIAS ? elem<DT, VEC>(bv[v], i) : 0.0f;
-                    out[v][i] = __builtin_fmaf(d * s, elem<DT, VEC>(wv[v], i), bias);
+                    for (int i = 0; i < VEC; ++i) {
+                        const float d = (elem<DT, VEC>(xv[v], i) - shift) - c;
+                        const float bias = BIAS ? elem<DT, VEC>(bv[v], i) : 0.0f;
+                        o[i] = __builtin_fmaf(d * scale, elem<DT, VEC>(wv[v], i), bias);
+                    }
+                    if (in_row(v)) store_raw<DT, VEC, NT>(yp, row_off + col_of(v), make_raw<DT, VEC>(o));
                 }
+            }
+            continue;
         }
-
+        if (valid) {
 #pragma unroll
-        for (int v = 0; v < VPT; ++v) {
-            const int64_t col = int64_t(v * LPR + lane) * VEC;
-            if (valid && (!MASKED || col < width))
-                store_raw<DT, VEC, NT>(yp, row_off + col, make_raw<DT, VEC>(out[v]));
+            for (int v = 0; v < VPT; ++v) {
+                R wr = wv[v];
+                if constexpr (DUAL) wr = second ? wv2[v] : wv[v];
+                float o[VEC];
+#pragma unroll
+                for (int i = 0; i < VEC; ++i)
+                    o[i] = (elem<DT, VEC>(xv[v], i) * scale) * elem<DT, VEC>(wr, i);
+                if (in_row(v)) store_raw<DT, VEC, NT>(yp, row_off + col_of(v), make_raw<DT, VEC>(o));
+            }
         }
     }
 }
@@ -250,15 +276,29 @@ __global__ __launch_bounds__(BLOCK) void norm_rows_wide(NormArgs a) {
     }
 }
 
-// Plain 16-byte-per-lane copy, the practical HBM ceiling the norms are
-// measured against (reads and writes the same bytes a norm does, with no
-// arithmetic).  `n16` = number of 16-byte packs.
-template <int BLOCK>
+// Plain copy, the practical HBM ceiling the norms are measured against (it
+// reads and writes the same bytes a one-pass norm does, with no
+// arithmetic).  Each thread moves U 16-byte packs per step (all loads
+// issued before the stores), with non-temporal accesses; `n16` = number of
+// 16-byte packs.
+template <int BLOCK, int U>
 __global__ __launch_bounds__(BLOCK) void copy16(const u32x4* __restrict__ src,
                                                 u32x4* __restrict__ dst, int64_t n16) {
-    for (int64_t i = int64_t(blockIdx.x) * BLOCK + threadIdx.x; i < n16;
-         i += int64_t(gridDim.x) * BLOCK)
-        dst[i] = src[i];
+    const int64_t step = int64_t(gridDim.x) * BLOCK * U;
+    for (int64_t base = int64_t(blockIdx.x) * BLOCK * U + threadIdx.x; base < n16;
+         base += step) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + int64_t(u) * BLOCK;
+            if (i < n16) v[u] = __builtin_nontemporal_load(src + i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + int64_t(u) * BLOCK;
+            if (i < n16) __builtin_nontemporal_store(v[u], dst + i);
+        }
+    }
 }
 
 }  // namespace fnorm

@@ -26,6 +26,7 @@ struct Variant {
     bool masked;        // handles width < lpr*vpt*vec (per-pack predicate)
     bool nt;            // non-temporal loads/stores of x and y
     bool wide;          // non-resident multi-pass kernel
+    int grid_cap;       // persistent grid: workgroups per CU (0 = as many as fit)
     int64_t capacity() const { return wide ? INT64_MAX : int64_t(lpr) * vpt * vec; }
     int rows_per_block() const { return wide ? 1 : block / lpr; }
 };
