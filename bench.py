@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_bf16_65536x4096_traffic.json")
-KERNEL_SOURCES = ["fnorm_device.hpp", "fnorm_kernels.hpp", "fnorm_instances.hpp"]
+KERNEL_SOURCES = ["fnorm_device.hpp", "fnorm_kernels.hpp", "fnorm_instances.hpp", "fnorm_api.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -55,6 +55,8 @@ def parse():
                    help="untimed steps; the GPU needs tens of ms of sustained load "
                         "before its clocks settle")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-composed", action="store_true",
+                   help="skip the fused-vs-composed ABBA comparison")
     p.add_argument("--ops", default="dual,rms,layer", help="subset of the step, for profiling")
     return p.parse_args()
 
@@ -186,6 +188,10 @@ def main():
                 "frac": round(dom["bytes"] / (dom["avg_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                 "traffic": traffic, "kernel": dominant}
 
+    composed = None
+    if not args.no_composed and len(plan) == 3:
+        composed = fused_vs_composed(trn, inputs, dev, stream, d, wl_rms, wl_ln, log)
+
     cpu = None
     if not args.no_cpu_baseline and len(plan) == 3:
         cpu = cpu_baseline(wl_dual, wl_rms, wl_ln, log)
@@ -202,9 +208,70 @@ def main():
                       "frac_peak_hbm": round(value / PEAK_HBM_GBS, 4),
                       "parallelism": "rows across workgroups (1 GPU)"},
            "per_op": per_op, "copy_ceiling": ceiling,
-           "roofline": roofline, "cpu_baseline": cpu,
+           "roofline": roofline, "cpu_baseline": cpu, "fused_vs_composed": composed,
            "wall_s_timed_region": round(wall, 4)}
     print(json.dumps(out), flush=True)
+
+
+def fused_vs_composed(trn, inputs, dev, stream, d, wl_rms, wl_ln, log):
+    """The pages' own experiment on this GPU: the fused kernel against the
+    same formula run one primitive per launch (6 launches for RMSNorm, 9 for
+    LayerNorm with bias), interleaved ABBA (the arm order flips every rep so
+    a drift cannot favour one arm), 30 reps, per-call time on the stream,
+    minimum and mean kept.  Shapes: the notebook's Part 1 RMSNorm input, the
+    kernel_micro_ab LayerNorm input, and the two large workloads."""
+    import torch
+
+    reps = 30
+    small_r = inputs.rms_f32_512x1024("iota")
+    small_l = inputs.layer_f32_1024x768()
+    cases = []
+    for name, wl, op in (("rms_f32_4x128x1024_iota", small_r, "rms"),
+                         ("layer_f32_1x1024x768", small_l, "layer"),
+                         ("rms_bf16_16384x8192", wl_rms, "rms"),
+                         ("layer_bf16_65536x4096", wl_ln, "layer")):
+        t = d.get(wl.name) or {k: v.to(dev) for k, v in wl.tensors.items() if torch.is_tensor(v)}
+        fused, comp, nbytes = _arms(trn, torch, op, t, wl.eps)
+        cases.append((name, fused, comp, nbytes))
+    out = {}
+    for name, fused, comp, nbytes in cases:
+        for f in (fused, comp, fused, comp):
+            f()
+        torch.cuda.synchronize()
+        times = {"fused": [], "composed": []}
+        for r in range(reps):
+            arms = (("fused", fused), ("composed", comp))
+            if r % 2:
+                arms = arms[::-1]
+            for arm, f in arms:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                f()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times[arm].append(e0.elapsed_time(e1) * 1e3)
+        rec = {arm: {"min_us": round(min(v), 2), "mean_us": round(sum(v) / len(v), 2)}
+               for arm, v in times.items()}
+        rec["speedup_min"] = round(rec["composed"]["min_us"] / rec["fused"]["min_us"], 2)
+        rec["fused_gbs"] = round(nbytes / (rec["fused"]["min_us"] * 1e-6) / 1e9, 1)
+        out[name] = rec
+        log(f"[bench] fused vs composed {name}: {rec}")
+        torch.cuda.empty_cache()
+    return out
+
+
+def _arms(trn, torch, op, t, eps):
+    """(fused call, composed call, algorithmic bytes) bound to these tensors."""
+    x, w, b = t["x"], t["w"], t.get("b")
+    y = torch.empty_like(x)
+    ws = trn.composed_workspace(trn.OP_RMS if op == "rms" else trn.OP_LAYER, x)
+    nbytes = 2 * x.numel() * x.element_size()
+    if op == "rms":
+        return (lambda: trn.rms_norm(x, w, eps, out=y),
+                lambda: trn.rms_norm_composed(x, w, eps, out=y, workspace=ws), nbytes)
+    return (lambda: trn.layer_norm(x, w, b, eps, out=y),
+            lambda: trn.layer_norm_composed(x, w, b, eps, out=y, workspace=ws), nbytes)
 
 
 def cpu_baseline(wl_dual, wl_rms, wl_ln, log):

@@ -51,7 +51,8 @@ typedef enum {
     FNORM_ERR_DTYPE = 4,       /* dtype not an fnorm_dtype */
     FNORM_ERR_ALIAS = 5,       /* an output overlaps another buffer (other than y == x) */
     FNORM_ERR_UNSUPPORTED = 6, /* no kernel for the request, or variant out of range */
-    FNORM_ERR_LAUNCH = 7       /* the HIP launch failed; fnorm_last_error() has the text */
+    FNORM_ERR_LAUNCH = 7,      /* the HIP launch failed; fnorm_last_error() has the text */
+    FNORM_ERR_WORKSPACE = 8    /* workspace NULL, misaligned, too small or overlapping */
 } fnorm_status;
 
 typedef enum { FNORM_OP_RMS = 0, FNORM_OP_LAYER = 1, FNORM_OP_DUAL = 2 } fnorm_op;
@@ -122,6 +123,29 @@ int fnorm_variant_count(int op, int dtype, int64_t width, int aligned);
  */
 int fnorm_describe(int op, int dtype, int64_t width, int aligned, int variant, char* buf,
                    int64_t len);
+
+/*
+ * Composed (unfused) baselines: the same RMSNorm / LayerNorm computed one
+ * primitive per launch, every intermediate going through HBM, the way a
+ * framework runs the textbook formula op by op.
+ *   RMSNorm (the composed cell of the Emily notebook, Part 1), 6 launches:
+ *     square, row mean, + eps, sqrt, divide x by the root, multiply by w.
+ *   LayerNorm (the `layer_norm` definition of the Emily.Fast docs), 9
+ *   launches (8 without bias): row mean, subtract, square, row mean, + eps,
+ *   sqrt, divide, multiply by w, add b.
+ * Intermediates are fp32 in the caller's `workspace` (device memory, 16-byte
+ * aligned, at least fnorm_composed_workspace_bytes(op, rows, width) bytes,
+ * not overlapping any tensor); the output has the input's type.  They exist
+ * to measure what fusion saves; they are checked against the same oracle.
+ * Other conventions as above; in place (y == x) is allowed.
+ */
+int64_t fnorm_composed_workspace_bytes(int op, int64_t rows, int64_t width);
+int fnorm_rms_composed(const void* x, const void* w, void* y, int64_t rows, int64_t width,
+                       float eps, int dtype, void* workspace, int64_t workspace_bytes,
+                       void* stream);
+int fnorm_layer_composed(const void* x, const void* w, const void* b, void* y, int64_t rows,
+                         int64_t width, float eps, int dtype, void* workspace,
+                         int64_t workspace_bytes, void* stream);
 
 /* Static text of a status code. */
 const char* fnorm_status_string(int status);

@@ -136,3 +136,23 @@ def test_every_resident_width_has_a_kernel():
                 assert trn.variant_count(trn.OP_RMS, dt, w, aligned) >= 4
                 assert trn.variant_count(trn.OP_LAYER, dt, w, aligned) >= 4
                 assert trn.variant_count(trn.OP_DUAL, dt, w, aligned) >= 2
+
+
+def test_composed_validation(lib):
+    W = 0x60000000
+    need = lib.fnorm_composed_workspace_bytes(0, 4, 8)
+    assert need >= 4 * 8 * 4
+    assert lib.fnorm_composed_workspace_bytes(1, 4, 8) > need
+    assert lib.fnorm_composed_workspace_bytes(2, 4, 8) == -1
+    assert lib.fnorm_composed_workspace_bytes(0, 4, 0) == -1
+    # workspace missing, too small, misaligned, overlapping
+    assert lib.fnorm_rms_composed(A, B, C, 4, 8, 1e-6, F32, None, need, None) == 8
+    assert lib.fnorm_rms_composed(A, B, C, 4, 8, 1e-6, F32, W, need - 1, None) == 8
+    assert lib.fnorm_rms_composed(A, B, C, 4, 8, 1e-6, F32, W + 4, need, None) == 8
+    assert lib.fnorm_rms_composed(A, B, C, 4, 8, 1e-6, F32, A, need, None) == 8
+    # the common checks apply too
+    assert lib.fnorm_rms_composed(A, B, C, -1, 8, 1e-6, F32, W, need, None) == 2
+    assert lib.fnorm_layer_composed(A, B, None, A + 16, 4, 8, 1e-6, F32, W, 1 << 20, None) == 5
+    assert lib.fnorm_layer_composed(A, None, None, C, 4, 8, 1e-6, F32, W, 1 << 20, None) == 1
+    assert lib.fnorm_rms_composed(None, None, None, 0, 8, 1e-6, BF16, None, 0, None) == 0
+    assert lib.fnorm_last_error() == b""

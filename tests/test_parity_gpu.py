@@ -359,3 +359,41 @@ def test_describe_matches_hot_configs():
     assert ".exact" in trn.describe(trn.OP_RMS, trn.BF16, 8192)
     assert ".exact" in trn.describe(trn.OP_LAYER, trn.BF16, 4096)
     assert ".exact" in trn.describe(trn.OP_DUAL, trn.BF16, 128)
+
+
+# ----------------------------------------------------------------- composed baselines
+COMPOSED_CASES = [("rms", torch.float32, 512, 1024), ("layer", torch.float32, 1024, 768),
+                  ("rms", torch.bfloat16, 1024, 8192), ("layer", torch.bfloat16, 2048, 4096),
+                  ("rms", torch.bfloat16, 37, 100), ("layer", torch.float32, 37, 1001),
+                  ("layer", torch.bfloat16, 64, 128), ("rms", torch.float32, 3, 7)]
+
+
+@pytest.mark.parametrize("op,dtype,rows,width", COMPOSED_CASES,
+                         ids=[f"{a}-{str(b)[6:]}-{c}x{d}" for a, b, c, d in COMPOSED_CASES])
+def test_composed_chain_matches_oracle(o, op, dtype, rows, width):
+    t = inputs.random_rows(op, rows, width, dtype, seed=rows + width, mean=0.5, std=1.5)
+    say(f"[composed] {op} {dtype} {rows}x{width}")
+    x, w = t["x"].to(DEV), t["w"].to(DEV)
+    if op == "rms":
+        y = trn.rms_norm_composed(x, w, 1e-5)
+    else:
+        y = trn.layer_norm_composed(x, w, t["b"].to(DEV), 1e-5)
+    torch.cuda.synchronize()
+    helpers.check(op, y.cpu(), run_oracle(o, op, t, 1e-5), t["w"], f"composed {op}")
+    if op == "layer":
+        y0 = trn.layer_norm_composed(x, w, None, 1e-5)
+        torch.cuda.synchronize()
+        t0 = {"x": t["x"], "w": t["w"]}
+        helpers.check(op, y0.cpu(), run_oracle(o, op, t0, 1e-5), t["w"], "composed no bias")
+
+
+def test_composed_iota_page_case(o):
+    """The notebook's Part 1 correctness input: composed and fused agree
+    closely (the page expects differences of order 1e-5)."""
+    wl = inputs.rms_f32_512x1024("iota")
+    x, w = wl.tensors["x"].to(DEV), wl.tensors["w"].to(DEV)
+    yc = trn.rms_norm_composed(x, w, wl.eps)
+    yf = trn.rms_norm(x, w, wl.eps)
+    torch.cuda.synchronize()
+    assert float((yc - yf).abs().max()) <= 1e-5
+    helpers.check("rms", yc.cpu(), run_oracle(o, "rms", wl.tensors, wl.eps), label="composed iota")

@@ -26,7 +26,7 @@ F32, BF16 = 0, 1
 OP_RMS, OP_LAYER, OP_DUAL = 0, 1, 2
 STATUS = {0: "FNORM_OK", 1: "FNORM_ERR_NULL", 2: "FNORM_ERR_SHAPE", 3: "FNORM_ERR_EPS",
           4: "FNORM_ERR_DTYPE", 5: "FNORM_ERR_ALIAS", 6: "FNORM_ERR_UNSUPPORTED",
-          7: "FNORM_ERR_LAUNCH"}
+          7: "FNORM_ERR_LAUNCH", 8: "FNORM_ERR_WORKSPACE"}
 
 
 class FnormError(RuntimeError):
@@ -54,6 +54,9 @@ _SIGNATURES = {
     "fnorm_last_error": ([], ctypes.c_char_p),
     "fnorm_version": ([], _I),
     "fnorm_bench_copy": ([_P, _P, _I64, _P], _I),
+    "fnorm_composed_workspace_bytes": ([_I, _I64, _I64], _I64),
+    "fnorm_rms_composed": ([_P, _P, _P, _I64, _I64, _F, _I, _P, _I64, _P], _I),
+    "fnorm_layer_composed": ([_P, _P, _P, _P, _I64, _I64, _F, _I, _P, _I64, _P], _I),
 }
 
 
@@ -187,6 +190,51 @@ def dual_head_rms_norm(q, k, qw, kw, eps: float = 1e-6, q_out=None, k_out=None,
                                        q.numel() // hd, k.numel() // hd, hd, eps, code,
                                        _stream(q), variant))
     return qy, ky
+
+
+def composed_workspace(op: int, x, device=None):
+    """A workspace tensor big enough for the composed chain on x."""
+    torch = _torch()
+    width = x.shape[-1]
+    n = lib().fnorm_composed_workspace_bytes(op, x.numel() // width, width)
+    if n < 0:
+        raise ValueError("invalid shape for the composed chain")
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=x.device if device is None else device)
+
+
+def rms_norm_composed(x, w, eps: float = 1e-6, out=None, workspace=None):
+    """Unfused baseline: RMSNorm as 6 launches (fp32 intermediates in `workspace`)."""
+    torch = _torch()
+    code = _dtype_code(x)
+    _require(x, "x", x.dtype, x.device)
+    _require(w, "w", x.dtype, x.device)
+    width = x.shape[-1]
+    if tuple(w.shape) != (width,):
+        raise ValueError(f"w has shape {tuple(w.shape)}, expected ({width},)")
+    y = torch.empty_like(x) if out is None else out
+    ws = composed_workspace(OP_RMS, x) if workspace is None else workspace
+    _check(lib().fnorm_rms_composed(_ptr(x), _ptr(w), _ptr(y), x.numel() // width, width, eps,
+                                    code, _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
+    return y
+
+
+def layer_norm_composed(x, w, b=None, eps: float = 1e-5, out=None, workspace=None):
+    """Unfused baseline: LayerNorm as 9 launches (8 without b)."""
+    torch = _torch()
+    code = _dtype_code(x)
+    _require(x, "x", x.dtype, x.device)
+    _require(w, "w", x.dtype, x.device)
+    width = x.shape[-1]
+    if tuple(w.shape) != (width,) or (b is not None and tuple(b.shape) != (width,)):
+        raise ValueError("w and b must have shape (width,)")
+    if b is not None:
+        _require(b, "b", x.dtype, x.device)
+    y = torch.empty_like(x) if out is None else out
+    ws = composed_workspace(OP_LAYER, x) if workspace is None else workspace
+    _check(lib().fnorm_layer_composed(_ptr(x), _ptr(w), _ptr(b), _ptr(y), x.numel() // width,
+                                      width, eps, code, _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream(x)))
+    return y
 
 
 def variant_count(op: int, dtype_code: int, width: int, aligned: bool = True) -> int:

@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "../../include/fnorm.h"
+#include "fnorm_composed.hpp"
 #include "fnorm_kernels.hpp"
 #include "fnorm_table.hpp"
 
@@ -67,7 +68,7 @@ struct Choice {
     bool persistent = true;
 };
 
-constexpr int kMaxCandidates = 24;
+constexpr int kMaxCandidates = 64;
 
 const Variant* smallest_masked(int kind, int dt, int vec, int64_t width) {
     const Variant* best = nullptr;
@@ -127,6 +128,8 @@ int op_kind(int op, bool has_bias) {
 
 void describe_choice(const Choice& c, char* buf, size_t len) {
     const Variant& v = *c.v;
+    static const char* nts[] = {"", ".ntst", ".ntld", ".nt"};
+    const char* nt = nts[(v.nt & NT_LOAD ? 2 : 0) | (v.nt & NT_STORE ? 1 : 0)];
     static const char* kinds[] = {"rms", "layer", "layer", "dual", "copy"};
     if (v.wide)
         std::snprintf(buf, len, "%s.%s.vec%d.wide.blk%d.%s", kinds[v.kind], dtype_name(v.dt),
@@ -134,12 +137,11 @@ void describe_choice(const Choice& c, char* buf, size_t len) {
     else if (c.persistent && v.grid_cap > 0)
         std::snprintf(buf, len, "%s.%s.vec%d.vpt%d.lpr%d.blk%d.%s%s.persistent%d", kinds[v.kind],
                       dtype_name(v.dt), v.vec, v.vpt, v.lpr, v.block,
-                      v.masked ? "masked" : "exact", v.nt ? ".nt" : "", v.grid_cap);
+                      v.masked ? "masked" : "exact", nt, v.grid_cap);
     else
         std::snprintf(buf, len, "%s.%s.vec%d.vpt%d.lpr%d.blk%d.%s%s.%s", kinds[v.kind],
                       dtype_name(v.dt), v.vec, v.vpt, v.lpr, v.block,
-                      v.masked ? "masked" : "exact", v.nt ? ".nt" : "",
-                      c.persistent ? "persistent" : "grid");
+                      v.masked ? "masked" : "exact", nt, c.persistent ? "persistent" : "grid");
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -349,8 +351,57 @@ const char* fnorm_status_string(int status) {
         case FNORM_ERR_ALIAS: return "FNORM_ERR_ALIAS: output overlaps another buffer";
         case FNORM_ERR_UNSUPPORTED: return "FNORM_ERR_UNSUPPORTED: no kernel for this request";
         case FNORM_ERR_LAUNCH: return "FNORM_ERR_LAUNCH: HIP launch failed";
+        case FNORM_ERR_WORKSPACE: return "FNORM_ERR_WORKSPACE: workspace missing, small or overlapping";
         default: return "unknown fnorm status";
     }
+}
+
+int64_t fnorm_composed_workspace_bytes(int op, int64_t rows, int64_t width) {
+    if ((op != FNORM_OP_RMS && op != FNORM_OP_LAYER) || rows < 0 || width <= 0) return -1;
+    if (rows > 0 && width > (INT64_MAX / 16) / rows) return -1;
+    return composed::workspace_bytes(op == FNORM_OP_LAYER, rows, width);
+}
+
+static int run_composed(const char* op, bool layer, const void* x, const void* w, const void* b,
+                        void* y, int64_t rows, int64_t width, float eps, int dtype,
+                        void* workspace, int64_t workspace_bytes, void* stream) {
+    if (int s = check_scalars(op, dtype, rows, width, eps)) return s;
+    if (rows == 0) return ok();
+    if (!x || !w || !y) return fail(FNORM_ERR_NULL, op, "x, w and y must be non-NULL");
+    const int64_t eb = elem_bytes(dtype);
+    const int64_t xb = rows * width * eb;
+    if (y != x && overlap(y, xb, x, xb))
+        return fail(FNORM_ERR_ALIAS, op, "y overlaps x without being equal to it");
+    if (overlap(y, xb, w, width * eb) || overlap(y, xb, b, width * eb))
+        return fail(FNORM_ERR_ALIAS, op, "y overlaps a weight");
+    const int64_t need = composed::workspace_bytes(layer, rows, width);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+        return fail(FNORM_ERR_WORKSPACE, op, "workspace must be 16-byte aligned and hold %lld bytes",
+                    (long long)need);
+    if (overlap(workspace, need, x, xb) || overlap(workspace, need, y, xb) ||
+        overlap(workspace, need, w, width * eb) || overlap(workspace, need, b, width * eb))
+        return fail(FNORM_ERR_WORKSPACE, op, "workspace overlaps a tensor");
+    const bool vec4 = width % 4 == 0 && aligned16(x) && aligned16(w) && aligned16(y) &&
+                      (!b || aligned16(b));
+    hipError_t e = composed::run(layer, x, w, b, y, rows, width, eps, dtype, vec4, workspace,
+                                 device_cus(), stream);
+    if (e != hipSuccess)
+        return fail(FNORM_ERR_LAUNCH, op, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int fnorm_rms_composed(const void* x, const void* w, void* y, int64_t rows, int64_t width,
+                       float eps, int dtype, void* workspace, int64_t workspace_bytes,
+                       void* stream) {
+    return run_composed("fnorm_rms_composed", false, x, w, nullptr, y, rows, width, eps, dtype,
+                        workspace, workspace_bytes, stream);
+}
+
+int fnorm_layer_composed(const void* x, const void* w, const void* b, void* y, int64_t rows,
+                         int64_t width, float eps, int dtype, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+    return run_composed("fnorm_layer_composed", true, x, w, b, y, rows, width, eps, dtype,
+                        workspace, workspace_bytes, stream);
 }
 
 const char* fnorm_last_error(void) { return g_err; }

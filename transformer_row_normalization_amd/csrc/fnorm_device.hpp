@@ -21,6 +21,7 @@ enum : int { DT_F32 = 0, DT_BF16 = 1 };
 enum : int { OP_RMS = 0, OP_LAYER = 1 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -28,6 +29,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 template <int DT, int VEC> struct Raw;
 template <> struct Raw<DT_F32, 4> { using type = u32x4; };
 template <> struct Raw<DT_BF16, 8> { using type = u32x4; };
+template <> struct Raw<DT_BF16, 4> { using type = u32x2; };
 template <> struct Raw<DT_F32, 1> { using type = uint32_t; };
 template <> struct Raw<DT_BF16, 1> { using type = uint16_t; };
 
@@ -39,6 +41,10 @@ template <int DT, int VEC>
 __device__ __forceinline__ typename Raw<DT, VEC>::type raw_zero() {
     return typename Raw<DT, VEC>::type(0);
 }
+
+// Cache policy of the row accesses: bit 0 = non-temporal (streaming) loads
+// of x, bit 1 = non-temporal stores of y.
+enum : int { NT_NONE = 0, NT_LOAD = 1, NT_STORE = 2, NT_BOTH = 3 };
 
 // Load the pack that starts at element `idx` of `base`.  NT selects the
 // non-temporal (streaming) cache policy.
@@ -74,7 +80,8 @@ __device__ __forceinline__ float elem(const typename Raw<DT, VEC>::type& r, int 
         const uint32_t u = r[i];
         return __builtin_bit_cast(float, u);
     } else {
-        return (i & 1) ? bf16_hi(r[i >> 1]) : bf16_lo(r[i >> 1]);
+        const uint32_t u = r[i >> 1];
+        return (i & 1) ? bf16_hi(u) : bf16_lo(u);
     }
 }
 
@@ -93,6 +100,8 @@ __device__ __forceinline__ typename Raw<DT, VEC>::type make_raw(const float (&f)
     } else if constexpr (DT == DT_F32) {
         return u32x4{__builtin_bit_cast(uint32_t, f[0]), __builtin_bit_cast(uint32_t, f[1]),
                      __builtin_bit_cast(uint32_t, f[2]), __builtin_bit_cast(uint32_t, f[3])};
+    } else if constexpr (VEC == 4) {
+        return u32x2{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
     } else {
         return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};

@@ -12,7 +12,7 @@
 
 namespace fnorm {
 
-template <int KIND, int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, bool NT>
+template <int KIND, int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, int NT>
 inline Variant make_variant(int cap) {
     constexpr int OP = (KIND == K_LAYER || KIND == K_LAYER_NOBIAS) ? OP_LAYER : OP_RMS;
     constexpr bool BIAS = KIND == K_LAYER;
@@ -33,7 +33,7 @@ inline Variant make_variant(int cap) {
     return v;
 }
 
-template <int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, bool NT>
+template <int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, int NT>
 inline void add_shape(std::vector<Variant>& t, int cap = 0) {
     t.push_back(make_variant<K_RMS, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
     t.push_back(make_variant<K_LAYER, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
@@ -53,7 +53,7 @@ inline Variant make_wide() {
     v.lpr = BLOCK;
     v.block = BLOCK;
     v.masked = true;
-    v.nt = false;
+    v.nt = NT_NONE;
     v.wide = true;
     v.grid_cap = 0;
     return v;
@@ -71,24 +71,24 @@ inline void add_wide(std::vector<Variant>& t) {
 // that are not a multiple of the pack).
 template <int DT, int V>
 inline void add_masked(std::vector<Variant>& t) {
-    add_shape<DT, V, 1, 1, 256, true, false>(t);
-    add_shape<DT, V, 1, 2, 256, true, false>(t);
-    add_shape<DT, V, 1, 4, 256, true, false>(t);
-    add_shape<DT, V, 1, 8, 256, true, false>(t);
-    add_shape<DT, V, 1, 16, 256, true, false>(t);
-    add_shape<DT, V, 1, 32, 256, true, false>(t);
-    add_shape<DT, V, 1, 64, 256, true, false>(t);
-    add_shape<DT, V, 2, 64, 256, true, false>(t);
-    add_shape<DT, V, 4, 64, 256, true, false>(t);
-    add_shape<DT, V, 8, 64, 256, true, false>(t);
-    add_shape<DT, V, 4, 256, 256, true, false>(t);
-    add_shape<DT, V, 8, 256, 256, true, false>(t);
-    add_shape<DT, V, 4, 1024, 1024, true, false>(t);
-    add_shape<DT, V, 8, 1024, 1024, true, false>(t);
+    add_shape<DT, V, 1, 1, 256, true, NT_NONE>(t);
+    add_shape<DT, V, 1, 2, 256, true, NT_NONE>(t);
+    add_shape<DT, V, 1, 4, 256, true, NT_NONE>(t);
+    add_shape<DT, V, 1, 8, 256, true, NT_NONE>(t);
+    add_shape<DT, V, 1, 16, 256, true, NT_NONE>(t);
+    add_shape<DT, V, 1, 32, 256, true, NT_NONE>(t);
+    add_shape<DT, V, 1, 64, 256, true, NT_NONE>(t);
+    add_shape<DT, V, 2, 64, 256, true, NT_NONE>(t);
+    add_shape<DT, V, 4, 64, 256, true, NT_NONE>(t);
+    add_shape<DT, V, 8, 64, 256, true, NT_NONE>(t);
+    add_shape<DT, V, 4, 256, 256, true, NT_NONE>(t);
+    add_shape<DT, V, 8, 256, 256, true, NT_NONE>(t);
+    add_shape<DT, V, 4, 1024, 1024, true, NT_NONE>(t);
+    add_shape<DT, V, 8, 1024, 1024, true, NT_NONE>(t);
 }
 
-// EXACT(VPT, LPR, BLOCK, NT, CAP): an exact shape with non-temporal x/y
-// accesses or not, and its persistent-grid cap in workgroups per CU.
+// EXACT(VPT, LPR, BLOCK, NT, CAP): an exact shape, its NT_* cache-policy
+// mask, and its persistent-grid cap in workgroups per CU.
 #define FNORM_EXACT(VPT, LPR, BLOCK, NT, CAP) add_shape<DT, V, VPT, LPR, BLOCK, false, NT>(t, CAP);
 
 // Preference order, measured on MI355X (cold HBM, bf16): the first entry of
@@ -100,46 +100,46 @@ template <int DT>
 inline void register_dtype(std::vector<Variant>& t) {
     constexpr int V = 16 / Elem<DT>::bytes;
     // 16 packs (bf16 128 / f32 64): one 16-lane group per row
-    FNORM_EXACT(1, 16, 256, true, 0)
-    FNORM_EXACT(1, 16, 256, false, 0)
+    FNORM_EXACT(1, 16, 256, NT_BOTH, 0)
+    FNORM_EXACT(1, 16, 256, NT_NONE, 0)
     // 32 packs
-    FNORM_EXACT(1, 32, 256, true, 0)
-    FNORM_EXACT(2, 16, 256, false, 0)
-    FNORM_EXACT(1, 32, 256, false, 0)
+    FNORM_EXACT(1, 32, 256, NT_BOTH, 0)
+    FNORM_EXACT(2, 16, 256, NT_NONE, 0)
+    FNORM_EXACT(1, 32, 256, NT_NONE, 0)
     // 64 packs
-    FNORM_EXACT(1, 64, 256, true, 0)
-    FNORM_EXACT(1, 64, 256, false, 0)
+    FNORM_EXACT(1, 64, 256, NT_BOTH, 0)
+    FNORM_EXACT(1, 64, 256, NT_NONE, 0)
     // 96 packs (bf16 768)
-    FNORM_EXACT(3, 32, 256, true, 0)
-    FNORM_EXACT(3, 32, 256, false, 0)
+    FNORM_EXACT(3, 32, 256, NT_BOTH, 0)
+    FNORM_EXACT(3, 32, 256, NT_NONE, 0)
     // 128 packs (bf16 1024)
-    FNORM_EXACT(2, 64, 256, true, 2)
-    FNORM_EXACT(2, 64, 256, false, 0)
+    FNORM_EXACT(2, 64, 256, NT_BOTH, 2)
+    FNORM_EXACT(2, 64, 256, NT_NONE, 0)
     // 192 packs (f32 768)
-    FNORM_EXACT(3, 64, 256, false, 0)
-    FNORM_EXACT(3, 64, 256, true, 2)
+    FNORM_EXACT(3, 64, 256, NT_NONE, 0)
+    FNORM_EXACT(3, 64, 256, NT_BOTH, 2)
     // 256 packs (f32 1024, bf16 2048)
-    FNORM_EXACT(2, 128, 256, true, 2)
-    FNORM_EXACT(4, 64, 256, false, 0)
-    FNORM_EXACT(4, 64, 256, true, 2)
-    FNORM_EXACT(1, 256, 256, true, 2)
+    FNORM_EXACT(2, 128, 256, NT_BOTH, 2)
+    FNORM_EXACT(4, 64, 256, NT_NONE, 0)
+    FNORM_EXACT(4, 64, 256, NT_BOTH, 2)
+    FNORM_EXACT(1, 256, 256, NT_BOTH, 2)
     // 512 packs (bf16 4096, f32 2048)
-    FNORM_EXACT(4, 128, 256, true, 2)
-    FNORM_EXACT(4, 128, 256, false, 2)
-    FNORM_EXACT(8, 64, 256, true, 0)
-    FNORM_EXACT(2, 256, 256, true, 2)
-    FNORM_EXACT(1, 512, 512, true, 2)
-    FNORM_EXACT(1, 512, 1024, true, 2)
+    FNORM_EXACT(4, 128, 256, NT_BOTH, 2)
+    FNORM_EXACT(4, 128, 256, NT_NONE, 2)
+    FNORM_EXACT(8, 64, 256, NT_BOTH, 0)
+    FNORM_EXACT(2, 256, 256, NT_BOTH, 2)
+    FNORM_EXACT(1, 512, 512, NT_BOTH, 2)
+    FNORM_EXACT(1, 512, 1024, NT_BOTH, 2)
     // 1024 packs (bf16 8192, f32 4096)
-    FNORM_EXACT(1, 1024, 1024, true, 2)
-    FNORM_EXACT(1, 1024, 1024, false, 2)
-    FNORM_EXACT(2, 512, 512, true, 2)
-    FNORM_EXACT(4, 256, 256, true, 2)
-    FNORM_EXACT(8, 128, 256, true, 2)
+    FNORM_EXACT(1, 1024, 1024, NT_BOTH, 2)
+    FNORM_EXACT(1, 1024, 1024, NT_NONE, 2)
+    FNORM_EXACT(2, 512, 512, NT_BOTH, 2)
+    FNORM_EXACT(4, 256, 256, NT_BOTH, 2)
+    FNORM_EXACT(8, 128, 256, NT_BOTH, 2)
     // 2048 packs (f32 8192, bf16 16384)
-    FNORM_EXACT(2, 1024, 1024, true, 2)
-    FNORM_EXACT(4, 512, 512, true, 2)
-    FNORM_EXACT(8, 256, 256, true, 2)
+    FNORM_EXACT(2, 1024, 1024, NT_BOTH, 2)
+    FNORM_EXACT(4, 512, 512, NT_BOTH, 2)
+    FNORM_EXACT(8, 256, 256, NT_BOTH, 2)
     add_masked<DT, V>(t);
     add_masked<DT, 1>(t);
     add_wide<DT, V>(t);

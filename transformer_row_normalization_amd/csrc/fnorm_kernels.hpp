@@ -53,8 +53,10 @@ struct NormArgs {
 };
 
 template <int OP, int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, bool BIAS,
-          bool DUAL, bool NT>
+          bool DUAL, int NT>
 __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
+    constexpr bool NT_LD = (NT & NT_LOAD) != 0;
+    constexpr bool NT_ST = (NT & NT_STORE) != 0;
     using R = typename Raw<DT, VEC>::type;
     static_assert(BLOCK % 64 == 0 && BLOCK % LPR == 0, "launch shape");
     constexpr int RPB = BLOCK / LPR;                 // rows per block-row
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
         R xv[VPT];
 #pragma unroll
         for (int v = 0; v < VPT; ++v)
-            xv[v] = in_row(v) ? load_raw<DT, VEC, NT>(xp, row_off + col_of(v))
+            xv[v] = in_row(v) ? load_raw<DT, VEC, NT_LD>(xp, row_off + col_of(v))
                               : raw_zero<DT, VEC>();
 
         // Row scalars: out = (x - shift) * scale * w + bias.
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
                         const float bias = BIAS ? elem<DT, VEC>(bv[v], i) : 0.0f;
                         o[i] = __builtin_fmaf(d * scale, elem<DT, VEC>(wv[v], i), bias);
                     }
-                    if (in_row(v)) store_raw<DT, VEC, NT>(yp, row_off + col_of(v), make_raw<DT, VEC>(o));
+                    if (in_row(v)) store_raw<DT, VEC, NT_ST>(yp, row_off + col_of(v), make_raw<DT, VEC>(o));
                 }
             }
             continue;
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
 #pragma unroll
                 for (int i = 0; i < VEC; ++i)
                     o[i] = (elem<DT, VEC>(xv[v], i) * scale) * elem<DT, VEC>(wr, i);
-                if (in_row(v)) store_raw<DT, VEC, NT>(yp, row_off + col_of(v), make_raw<DT, VEC>(o));
+                if (in_row(v)) store_raw<DT, VEC, NT_ST>(yp, row_off + col_of(v), make_raw<DT, VEC>(o));
             }
         }
     }

@@ -24,7 +24,7 @@ struct Variant {
     int lpr;            // threads per row
     int block;          // threads per workgroup
     bool masked;        // handles width < lpr*vpt*vec (per-pack predicate)
-    bool nt;            // non-temporal loads/stores of x and y
+    int nt;             // NT_* mask: non-temporal loads of x / stores of y
     bool wide;          // non-resident multi-pass kernel
     int grid_cap;       // persistent grid: workgroups per CU (0 = as many as fit)
     int64_t capacity() const { return wide ? INT64_MAX : int64_t(lpr) * vpt * vec; }
