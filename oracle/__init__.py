@@ -63,6 +63,14 @@ class Oracle:
         lib.oracle_dual_head_rms.argtypes = [_P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64,
                                              ctypes.c_float, _P, _P]
         lib.oracle_dual_head_rms.restype = None
+        lib.oracle_rope_rows.argtypes = [_P, _I64, _I64, _I64, _I64, ctypes.c_int,
+                                         ctypes.c_float, ctypes.c_float, _I64, _P]
+        lib.oracle_rope_rows.restype = None
+        lib.oracle_dual_head_rms_rope.argtypes = [_P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64,
+                                                  _I64, ctypes.c_float, _I64, ctypes.c_int,
+                                                  ctypes.c_float, ctypes.c_float, _I64, _P, _P,
+                                                  _P]
+        lib.oracle_dual_head_rms_rope.restype = None
         self._lib = lib
 
     @staticmethod
@@ -129,6 +137,45 @@ class Oracle:
         self._lib.oracle_dual_head_rms(self._ptr(q), self._ptr(k), self._ptr(qw), self._ptr(kw),
                                        code, q.size // hd, k.size // hd, hd,
                                        ctypes.c_float(eps), self._ptr(qy), self._ptr(ky))
+        return qy, ky
+
+
+    def rope_rows(self, v: np.ndarray, heads: int, dims: int, traditional: bool, base: float,
+                  scale: float, offset: int, freqs: np.ndarray | None = None) -> np.ndarray:
+        """Rotary embedding of fp64 head vectors v [rows, head_dim] (a copy is
+        rotated and returned); row r is token r // heads."""
+        out = np.array(v, dtype=np.float64, order="C", copy=True)
+        hd = out.shape[-1]
+        rows = out.size // hd
+        if dims % 2 or not 2 <= dims <= hd:
+            raise ValueError("dims must be even, 2 <= dims <= head_dim")
+        fr = None if freqs is None else np.ascontiguousarray(freqs, dtype=np.float32)
+        if fr is not None and fr.shape != (dims // 2,):
+            raise ValueError("freqs must have dims/2 entries")
+        self._lib.oracle_rope_rows(self._ptr(out), rows, heads, hd, dims, int(traditional),
+                                   ctypes.c_float(base), ctypes.c_float(scale), offset,
+                                   self._ptr(fr))
+        return out
+
+    def dual_head_rms_rope(self, q, k, qw, kw, eps, dims, traditional, base, scale, offset,
+                           freqs=None):
+        """Dual head RMSNorm then rotary embedding; q [tokens, q_heads, hd],
+        k [tokens, k_heads, hd]; returns (queries, keys) in float64."""
+        q = np.ascontiguousarray(q)
+        k = np.ascontiguousarray(k)
+        code = self._dtype_code(q)
+        tokens, qh, hd = q.shape
+        kh = k.shape[1]
+        if k.shape[0] != tokens or k.shape[2] != hd:
+            raise ValueError("q and k must share tokens and head_dim")
+        fr = None if freqs is None else np.ascontiguousarray(freqs, dtype=np.float32)
+        qy = np.empty(q.shape, np.float64)
+        ky = np.empty(k.shape, np.float64)
+        self._lib.oracle_dual_head_rms_rope(
+            self._ptr(q), self._ptr(k), self._ptr(np.ascontiguousarray(qw)),
+            self._ptr(np.ascontiguousarray(kw)), code, tokens, qh, kh, hd, ctypes.c_float(eps),
+            dims, int(traditional), ctypes.c_float(base), ctypes.c_float(scale), offset,
+            self._ptr(fr), self._ptr(qy), self._ptr(ky))
         return qy, ky
 
 

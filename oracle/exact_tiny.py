@@ -76,3 +76,24 @@ def rms(rows: Sequence[Sequence[float]], w, eps) -> list[list[float]]:
 
 def layer(rows: Sequence[Sequence[float]], w, b, eps) -> list[list[float]]:
     return [layer_row(r, w, b, eps) for r in rows]
+
+
+def rope_row_complex(x, pos, dims, traditional, base, scale, freqs=None):
+    """Rotary embedding of one head vector written as complex multiplication:
+    pair i is the complex number z_i = x_a + 1j * x_b (a, b the pair's
+    indices: (i, i + dims/2) split-half, (2i, 2i + 1) interleaved), and
+    the result is z_i * exp(1j * theta_i) with theta_i = pos * scale *
+    inv_freq_i, inv_freq_i = base ** (-2 i / dims) or freqs[i] (Emily.Fast
+    docs, `rope` and `rope_with_freqs`).  Features past `dims` pass through.
+    Plain Python floats and cmath."""
+    import cmath
+
+    out = list(x)
+    half = dims // 2
+    for i in range(half):
+        inv = float(freqs[i]) if freqs is not None else float(base) ** (-2.0 * i / dims)
+        theta = pos * float(scale) * inv
+        a, b = (2 * i, 2 * i + 1) if traditional else (i, i + half)
+        z = complex(x[a], x[b]) * cmath.exp(1j * theta)
+        out[a], out[b] = z.real, z.imag
+    return out

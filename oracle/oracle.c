@@ -29,6 +29,20 @@
  *    comparison with a bf16 or fp32 output happens in the tests.
  *  - A NULL bias means a zero bias.
  *
+ * Rotary position embedding (Emily.Fast docs, sections `rope` and
+ * `rope_with_freqs`), applied after the dual head RMSNorm:
+ *  - angle of pair i of a head vector at position p:
+ *      theta_i = p * scale * inv_freq_i,  inv_freq_i = base^(-2i/dims)
+ *    (the geometric-progression schedule), or inv_freq_i = freqs[i] when an
+ *    inverse-frequency table of dims/2 entries is given;
+ *  - p = offset + token index (the scalar offset of the docs);
+ *  - pairs: split-half (i, i + dims/2) by default, paired-interleave
+ *    (2i, 2i + 1) when `traditional`; a pair (a, b) becomes
+ *      (a cos - b sin, b cos + a sin);
+ *  - only the first `dims` features of a head vector rotate, the rest pass
+ *    through (the docs' "trailing dims" read as the rotated feature count
+ *    of the last axis).
+ *
  * Element types: 0 = IEEE binary32, 1 = bfloat16 (the upper 16 bits of a
  * binary32).  Both widen to double without rounding.
  *
@@ -130,4 +144,53 @@ void oracle_dual_head_rms(const void *q, const void *k, const void *qw,
 {
     oracle_rms(q, qw, dtype, q_rows, head_dim, eps, qy);
     oracle_rms(k, kw, dtype, k_rows, head_dim, eps, ky);
+}
+
+/*
+ * Rotary position embedding of fp64 head vectors, in place (Emily.Fast docs,
+ * `rope` / `rope_with_freqs`).  v holds rows = tokens * heads vectors of
+ * head_dim; row r belongs to token r / heads.  freqs (dims/2 fp32 inverse
+ * frequencies) may be NULL, then base gives the schedule.
+ */
+void oracle_rope_rows(double *v, int64_t rows, int64_t heads, int64_t head_dim,
+                      int64_t dims, int traditional, float base, float scale,
+                      int64_t offset, const float *freqs)
+{
+    const int64_t half = dims / 2;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double pos = (double)(offset + r / heads);
+        double *x = v + r * head_dim;
+        for (int64_t i = 0; i < half; ++i) {
+            double inv_freq = freqs ? (double)freqs[i]
+                                    : pow((double)base, -2.0 * (double)i / (double)dims);
+            double theta = pos * (double)scale * inv_freq;
+            double c = cos(theta), s = sin(theta);
+            int64_t a = traditional ? 2 * i : i;
+            int64_t b = traditional ? 2 * i + 1 : i + half;
+            double xa = x[a], xb = x[b];
+            x[a] = xa * c - xb * s;
+            x[b] = xb * c + xa * s;
+        }
+    }
+}
+
+/*
+ * The dual head RMSNorm followed by the rotary embedding of both outputs:
+ * queries q [tokens, q_heads, head_dim], keys k [tokens, k_heads, head_dim],
+ * the same positions for both (mlx-c-rust `compile/norm_fusion.rs` for the
+ * dual norm; Emily.Fast `rope` for the rotation).
+ */
+void oracle_dual_head_rms_rope(const void *q, const void *k, const void *qw,
+                               const void *kw, int dtype, int64_t tokens,
+                               int64_t q_heads, int64_t k_heads, int64_t head_dim,
+                               float eps, int64_t dims, int traditional, float base,
+                               float scale, int64_t offset, const float *freqs,
+                               double *qy, double *ky)
+{
+    oracle_dual_head_rms(q, k, qw, kw, dtype, tokens * q_heads, tokens * k_heads,
+                         head_dim, eps, qy, ky);
+    oracle_rope_rows(qy, tokens * q_heads, q_heads, head_dim, dims, traditional, base,
+                     scale, offset, freqs);
+    oracle_rope_rows(ky, tokens * k_heads, k_heads, head_dim, dims, traditional, base,
+                     scale, offset, freqs);
 }

@@ -60,6 +60,30 @@ def main():
                   "source": "Emily.Fast docs, layer_norm (eps inside the square root)",
                   "x": xw, "w": w, "b": b, "eps_f32": 0.25,
                   "y": exact_tiny.layer(xw, w, b, 0.25)})
+    # Emily.Fast docs, `rope` example: x = iota({1, 1, 4, 8}) (4 positions of
+    # an 8-wide head), offset 0, dims 8, default base 10000 and scale 1; both
+    # pair layouts; and the `rope_with_freqs` example table [1, .1, .01, .001].
+    xs = [[float(r * 8 + j) for j in range(8)] for r in range(4)]
+    for trad in (False, True):
+        cases.append({"name": f"rope_doc_example_{'interleaved' if trad else 'split'}",
+                      "op": "rope", "source": "Emily.Fast docs, rope, Examples",
+                      "x": xs, "dims": 8, "traditional": trad, "base": 10000.0,
+                      "scale": 1.0, "offset": 0, "freqs": None,
+                      "y": [exact_tiny.rope_row_complex(row, p, 8, trad, 10000.0, 1.0)
+                            for p, row in enumerate(xs)]})
+    fr = [f32(1.0), f32(0.1), f32(0.01), f32(0.001)]
+    cases.append({"name": "rope_with_freqs_doc_example", "op": "rope",
+                  "source": "Emily.Fast docs, rope_with_freqs, Examples",
+                  "x": xs, "dims": 8, "traditional": False, "base": 10000.0, "scale": 1.0,
+                  "offset": 0, "freqs": fr,
+                  "y": [exact_tiny.rope_row_complex(row, p, 8, False, 10000.0, 1.0, fr)
+                        for p, row in enumerate(xs)]})
+    cases.append({"name": "rope_offset_scale_partial_dims", "op": "rope",
+                  "source": "Emily.Fast docs, rope (offset, scale, dims)",
+                  "x": xs, "dims": 4, "traditional": False, "base": 500.0, "scale": 0.5,
+                  "offset": 37, "freqs": None,
+                  "y": [exact_tiny.rope_row_complex(row, 37 + p, 4, False, 500.0, 0.5)
+                        for p, row in enumerate(xs)]})
     with open(os.path.join(HERE, "hand_cases.json"), "w") as f:
         json.dump({"generated_by": "tests/golden/make_golden.py (oracle/exact_tiny.py)",
                    "cases": cases}, f, indent=1)

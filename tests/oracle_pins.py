@@ -23,6 +23,14 @@ What pins what:
   bf16 decoding          hand-built bf16 bit patterns decode to the values
                          the format defines
   dual q/k               each half against exact brute force, queries first
+  RoPE                   golden values of the `rope` / `rope_with_freqs` doc
+                         inputs from a complex-number formulation
+                         (oracle/exact_tiny.py), norm preservation, identity
+                         at position 0, relative-position invariance,
+                         composition of offsets, scale as a position
+                         multiplier, interleaved = permuted split-half, an
+                         exact inverse-frequency table = the schedule,
+                         features past dims unchanged, dual + RoPE
 """
 from __future__ import annotations
 
@@ -67,6 +75,12 @@ def pin_golden_hand_cases(o):
     with open(GOLDEN) as f:
         cases = json.load(f)["cases"]
     for c in cases:
+        if c["op"] == "rope":
+            fr = None if c["freqs"] is None else np.array(c["freqs"], np.float32)
+            got = o.rope_rows(np.array(c["x"], np.float64), 1, c["dims"], c["traditional"],
+                              c["base"], c["scale"], c["offset"], fr)
+            _close(got, np.array(c["y"]), 1e-13, floor=1e-12, what=c["name"])
+            continue
         x = np.array(c["x"], dtype=np.float32)
         w = np.array(c["w"], dtype=np.float32)
         exp = np.array(c["y"], dtype=np.float64)
@@ -237,7 +251,98 @@ def pin_dual(o):
                floor=1e-300, what=f"dual keys {dtype}")
 
 
+# ------------------------------------------------------------------ RoPE
+def _rope_input(rng, rows, hd):
+    return rng.standard_normal((rows, hd))
+
+
+def pin_rope_norm_and_identity(o):
+    rng = np.random.default_rng(1101)
+    v = _rope_input(rng, 12, 16)
+    for trad in (False, True):
+        y = o.rope_rows(v, 3, 16, trad, 10000.0, 1.0, 5)
+        _close(np.linalg.norm(y, axis=1), np.linalg.norm(v, axis=1), 1e-14, what="rope norm")
+        y0 = o.rope_rows(v, 12, 16, trad, 10000.0, 1.0, 0)      # every row at position 0
+        assert np.array_equal(y0, v), "rope at position 0 is the identity"
+        # each rotated pair keeps its own length
+        y = o.rope_rows(v, 1, 16, trad, 300.0, 1.0, 2)
+        a = np.arange(8) * 2 if trad else np.arange(8)
+        b = a + 1 if trad else a + 8
+        _close(y[:, a] ** 2 + y[:, b] ** 2, v[:, a] ** 2 + v[:, b] ** 2, 1e-13,
+               what="rope pair length")
+
+
+def pin_rope_relative_position(o):
+    # <rope(a, p), rope(b, p + k)> depends only on k
+    rng = np.random.default_rng(1102)
+    a, b = _rope_input(rng, 1, 32), _rope_input(rng, 1, 32)
+    for trad in (False, True):
+        ref = None
+        for p in (0, 3, 100):
+            ra = o.rope_rows(a, 1, 32, trad, 10000.0, 1.0, p)
+            rb = o.rope_rows(b, 1, 32, trad, 10000.0, 1.0, p + 7)
+            d = float((ra @ rb.T)[0, 0])
+            ref = d if ref is None else ref
+            assert abs(d - ref) < 1e-12 * (1 + abs(ref)), "rope relative position"
+
+
+def pin_rope_composition_and_scale(o):
+    rng = np.random.default_rng(1103)
+    v = _rope_input(rng, 6, 16)
+    for trad in (False, True):
+        once = o.rope_rows(v, 6, 16, trad, 10000.0, 1.0, 9)      # one token: position = offset
+        twice = o.rope_rows(o.rope_rows(v, 6, 16, trad, 10000.0, 1.0, 4), 6, 16, trad,
+                            10000.0, 1.0, 5)
+        _close(twice, once, 1e-13, floor=1e-12, what="rope composition")
+        s2 = o.rope_rows(v, 6, 16, trad, 10000.0, 2.0, 9)
+        p2 = o.rope_rows(v, 6, 16, trad, 10000.0, 1.0, 18)
+        _close(s2, p2, 1e-13, floor=1e-12, what="rope scale multiplies the position")
+
+
+def pin_rope_layouts_and_table(o):
+    rng = np.random.default_rng(1104)
+    v = _rope_input(rng, 8, 16)
+    # interleaved pairs (2i, 2i+1) are the split-half pairs (i, i+8) after
+    # gathering the even then the odd features
+    perm = np.concatenate([np.arange(0, 16, 2), np.arange(1, 16, 2)])
+    trad = o.rope_rows(v, 2, 16, True, 10000.0, 1.0, 3)
+    split = o.rope_rows(v[:, perm], 2, 16, False, 10000.0, 1.0, 3)
+    _close(split, trad[:, perm], 1e-14, floor=1e-12, what="rope layouts")
+    # base 16 over 8 dims has inverse frequencies 16^(-2i/8) = 2^-i exactly
+    table = np.array([1, .5, .25, .125], np.float32)
+    for trad in (False, True):
+        tab8 = o.rope_rows(v[:, :8], 2, 8, trad, 1.0, 1.0, 3, table)
+        sch8 = o.rope_rows(v[:, :8], 2, 8, trad, 16.0, 1.0, 3)
+        assert np.array_equal(tab8, sch8), "rope table equals the schedule"
+    # features past dims pass through unchanged
+    p = o.rope_rows(v, 2, 6, False, 10000.0, 1.0, 3)
+    assert np.array_equal(p[:, 6:], v[:, 6:]), "rope tail"
+
+
+def pin_dual_rope(o):
+    rng = np.random.default_rng(1105)
+    for dtype in ("f32", "bf16"):
+        (q, qw, _), _ = _tiny_rows(rng, dtype, 16, 6)
+        (k, kw, _), _ = _tiny_rows(rng, dtype, 16, 3)
+        q3, k3 = q.reshape(3, 2, 16), k.reshape(3, 1, 16)
+        plain_q, plain_k = o.dual_head_rms(q3, k3, qw, kw, f32(1e-6))
+        for trad in (False, True):
+            fq, fk = o.dual_head_rms_rope(q3, k3, qw, kw, f32(1e-6), 16, trad, 10000.0, 1.0, 0)
+            # token 0 sits at position 0: unrotated
+            assert np.array_equal(fq[0], plain_q[0]) and np.array_equal(fk[0], plain_k[0])
+            # rotation keeps each head vector's length
+            _close(np.linalg.norm(fq, axis=2), np.linalg.norm(plain_q, axis=2), 1e-13,
+                   what="dual rope q norm")
+            _close(np.linalg.norm(fk, axis=2), np.linalg.norm(plain_k, axis=2), 1e-13,
+                   what="dual rope k norm")
+            # the keys of token t rotate like a query head of token t
+            fq2, fk2 = o.dual_head_rms_rope(q3, k3, qw, kw, f32(1e-6), 16, trad, 10000.0, 1.0, 4)
+            rk = o.rope_rows(plain_k.reshape(3, 16), 1, 16, trad, 10000.0, 1.0, 4)
+            _close(fk2.reshape(3, 16), rk, 1e-14, floor=1e-12, what="dual rope keys")
+
+
 PINS = [pin_golden_hand_cases, pin_exact_bruteforce_rms, pin_exact_bruteforce_layer,
         pin_rms_unit_invariant, pin_layer_moments, pin_library_identities,
         pin_special_cases, pin_invariances, pin_affine_structure, pin_row_independence,
-        pin_bf16_decoding, pin_dual]
+        pin_bf16_decoding, pin_dual, pin_rope_norm_and_identity, pin_rope_relative_position,
+        pin_rope_composition_and_scale, pin_rope_layouts_and_table, pin_dual_rope]

@@ -51,6 +51,28 @@ MUTANTS = {
                              "oracle_rms(k, qw, dtype, k_rows, head_dim, eps, ky);"),
     "dual_eps_dropped_for_keys": ("oracle_rms(k, kw, dtype, k_rows, head_dim, eps, ky);",
                                   "oracle_rms(k, kw, dtype, k_rows, head_dim, 0.0f, ky);"),
+    "rope_sign": ("x[a] = xa * c - xb * s;", "x[a] = xa * c + xb * s;"),
+    "rope_cos_sin_swapped": ("double c = cos(theta), s = sin(theta);",
+                             "double c = sin(theta), s = cos(theta);"),
+    "rope_no_offset": ("const double pos = (double)(offset + r / heads);",
+                       "const double pos = (double)(r / heads);"),
+    "rope_position_per_row": ("const double pos = (double)(offset + r / heads);",
+                              "const double pos = (double)(offset + r);"),
+    "rope_exponent_head_dim": ("pow((double)base, -2.0 * (double)i / (double)dims)",
+                               "pow((double)base, -2.0 * (double)i / (double)head_dim)"),
+    "rope_exponent_no_two": ("pow((double)base, -2.0 * (double)i / (double)dims)",
+                             "pow((double)base, -1.0 * (double)i / (double)dims)"),
+    "rope_no_scale": ("double theta = pos * (double)scale * inv_freq;",
+                      "double theta = pos * inv_freq;"),
+    "rope_split_pairs_adjacent": ("int64_t b = traditional ? 2 * i + 1 : i + half;",
+                                  "int64_t b = traditional ? 2 * i + 1 : half - 1 - i + half;"),
+    "rope_interleave_as_split": ("int64_t a = traditional ? 2 * i : i;",
+                                 "int64_t a = i;"),
+    "rope_freqs_ignored": ("double inv_freq = freqs ? (double)freqs[i]",
+                           "double inv_freq = 0 ? (double)freqs[i]"),
+    "dual_rope_keys_use_query_heads": (
+        "oracle_rope_rows(ky, tokens * k_heads, k_heads,",
+        "oracle_rope_rows(ky, tokens * k_heads, q_heads,"),
 }
 
 
