@@ -189,8 +189,10 @@ def main():
                 "traffic": traffic, "kernel": dominant}
 
     composed = None
+    rope = None
     if not args.no_composed and len(plan) == 3:
         composed = fused_vs_composed(trn, inputs, dev, stream, d, wl_rms, wl_ln, log)
+        rope = dual_rope_leg(trn, dq, qy, ky, wl_dual.eps, stream, log)
 
     cpu = None
     if not args.no_cpu_baseline and len(plan) == 3:
@@ -209,6 +211,7 @@ def main():
                       "parallelism": "rows across workgroups (1 GPU)"},
            "per_op": per_op, "copy_ceiling": ceiling,
            "roofline": roofline, "cpu_baseline": cpu, "fused_vs_composed": composed,
+           "dual_rope": rope,
            "wall_s_timed_region": round(wall, 4)}
     print(json.dumps(out), flush=True)
 
@@ -258,6 +261,37 @@ def fused_vs_composed(trn, inputs, dev, stream, d, wl_rms, wl_ln, log):
         out[name] = rec
         log(f"[bench] fused vs composed {name}: {rec}")
         torch.cuda.empty_cache()
+    return out
+
+
+def dual_rope_leg(trn, dq, qy, ky, eps, stream, log):
+    """The dual workload with the rotary embedding fused into the same launch
+    (positions 0..4095, base 10000, split-half) against the plain dual norm,
+    ABBA-interleaved, 30 reps; the rotation adds no HBM traffic."""
+    import torch
+
+    arms = {"dual": lambda: trn.dual_head_rms_norm(dq["q"], dq["k"], dq["qw"], dq["kw"], eps,
+                                                   q_out=qy, k_out=ky),
+            "dual_rope": lambda: trn.dual_head_rms_rope(dq["q"], dq["k"], dq["qw"], dq["kw"], eps,
+                                                        q_out=qy, k_out=ky)}
+    for f in arms.values():
+        f()
+    torch.cuda.synchronize()
+    times = {k: [] for k in arms}
+    for r in range(30):
+        order = list(arms) if r % 2 == 0 else list(arms)[::-1]
+        for k in order:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            arms[k]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[k].append(e0.elapsed_time(e1) * 1e3)
+    nbytes = 2 * (dq["q"].numel() + dq["k"].numel()) * 2
+    out = {k: {"min_us": round(min(v), 2), "mean_us": round(sum(v) / len(v), 2),
+               "gbs_min": round(nbytes / (min(v) * 1e-6) / 1e9, 1)} for k, v in times.items()}
+    out["kernel"] = trn.describe_rope(trn.BF16, 128, 128, False)
+    log(f"[bench] dual + rope: {out}")
     return out
 
 

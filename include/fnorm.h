@@ -95,6 +95,34 @@ int fnorm_dual_head_rms(const void* q, const void* k, const void* qw, const void
                         int dtype, void* stream);
 
 /*
+ * Dual q/k head RMSNorm fused with the rotary position embedding (RoPE) of
+ * both outputs, in one launch: qy = RoPE(RMSNorm(q, qw)), ky =
+ * RoPE(RMSNorm(k, kw)), rounded once.  RoPE follows the Emily.Fast docs,
+ * sections `rope` and `rope_with_freqs`: pair i of a head vector of token t
+ * rotates by theta_i = (offset + t) * scale * inv_freq_i, with inv_freq_i =
+ * base^(-2i / rope_dims), or freqs[i] when `freqs` (a DEVICE array of
+ * rope_dims/2 fp32 inverse frequencies) is given; pairs are
+ * (i, i + rope_dims/2) when traditional == 0 (split-half) and (2i, 2i + 1)
+ * when traditional != 0 (interleaved); features at or past rope_dims pass
+ * through.  Layout: q, qy [tokens, q_heads, head_dim]; k, ky
+ * [tokens, k_heads, head_dim]; both share the positions.
+ * rope_dims must be even, 2 <= rope_dims <= head_dim; base finite and > 0
+ * (unless freqs), scale finite, offset >= 0; else FNORM_ERR_SHAPE.
+ * Head shapes whose pair partners the kernel cannot reach (some partial
+ * rope_dims on wide heads) return FNORM_ERR_UNSUPPORTED.
+ */
+int fnorm_dual_head_rms_rope(const void* q, const void* k, const void* qw, const void* kw,
+                             void* qy, void* ky, int64_t tokens, int64_t q_heads,
+                             int64_t k_heads, int64_t head_dim, float eps, int64_t rope_dims,
+                             int traditional, float base, float scale, int64_t offset,
+                             const float* freqs, int dtype, void* stream);
+int fnorm_dual_head_rms_rope_v(const void* q, const void* k, const void* qw, const void* kw,
+                               void* qy, void* ky, int64_t tokens, int64_t q_heads,
+                               int64_t k_heads, int64_t head_dim, float eps, int64_t rope_dims,
+                               int traditional, float base, float scale, int64_t offset,
+                               const float* freqs, int dtype, void* stream, int variant);
+
+/*
  * Same calls with an explicit kernel variant: variant -1 is the default
  * choice (what the calls above use); 0 .. fnorm_variant_count()-1 force one
  * of the kernels able to serve the request (for testing every instance and
@@ -146,6 +174,12 @@ int fnorm_rms_composed(const void* x, const void* w, void* y, int64_t rows, int6
 int fnorm_layer_composed(const void* x, const void* w, const void* b, void* y, int64_t rows,
                          int64_t width, float eps, int dtype, void* workspace,
                          int64_t workspace_bytes, void* stream);
+
+/* Variant count and kernel name of the fused dual norm + RoPE, as above. */
+int fnorm_rope_variant_count(int dtype, int64_t head_dim, int64_t rope_dims, int traditional,
+                             int aligned);
+int fnorm_describe_rope(int dtype, int64_t head_dim, int64_t rope_dims, int traditional,
+                        int aligned, int variant, char* buf, int64_t len);
 
 /* Static text of a status code. */
 const char* fnorm_status_string(int status);

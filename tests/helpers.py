@@ -9,6 +9,8 @@ relative):
                                               (x - mean) * s * w + b can cancel)
   bf16 also    ulp distance between y and RNE_bf16(r) <= 1 (for LayerNorm
                where |r| >= |w_j|)
+  RoPE outputs a rotated pair (a, b) can cancel too: the floor of both
+               features is max(|w_a|, |w_b|), the scale of a normalized pair
 """
 from __future__ import annotations
 
@@ -78,12 +80,15 @@ def rel_err(y: np.ndarray, r: np.ndarray, floor: np.ndarray | None = None) -> np
 
 
 def check(op: str, y: torch.Tensor, r: np.ndarray, w: torch.Tensor | None = None,
-          label: str = "") -> dict:
+          label: str = "", floor: np.ndarray | None = None) -> dict:
     """Assert the tolerance for one output tensor against the fp64 oracle.
-    Returns the measured error figures."""
+    `floor` (broadcast to r's shape) replaces |w_j| as the error floor where
+    the output can cancel (LayerNorm, rotations).  Returns the measured
+    error figures."""
     yd = widen(y).reshape(r.shape)
-    floor = None
-    if op == "layer":
+    if floor is not None:
+        floor = np.broadcast_to(np.abs(floor), r.shape)
+    elif op == "layer":
         floor = np.broadcast_to(widen(w), r.shape)
     err = rel_err(yd, r, floor)
     nan_mismatch = int(np.sum(np.isnan(yd) != np.isnan(r)))
@@ -96,7 +101,7 @@ def check(op: str, y: torch.Tensor, r: np.ndarray, w: torch.Tensor | None = None
     else:
         assert out["max_rel"] <= BF16_REL_TOL, f"{label}: bf16 rel err {out['max_rel']:.3e}"
         ulps = ulp_distance_bf16(bf16_bits(y).reshape(r.shape), rne_bf16_bits(r))
-        if op == "layer":
+        if floor is not None:
             mask = np.abs(r) >= np.abs(floor)
             ulps = np.where(mask, ulps, 0)
         finite = np.isfinite(r)

@@ -156,3 +156,34 @@ def test_composed_validation(lib):
     assert lib.fnorm_layer_composed(A, None, None, C, 4, 8, 1e-6, F32, W, 1 << 20, None) == 1
     assert lib.fnorm_rms_composed(None, None, None, 0, 8, 1e-6, BF16, None, 0, None) == 0
     assert lib.fnorm_last_error() == b""
+
+
+def test_rope_validation(lib):
+    D, E, F = 0x1000000, 0x2000000, 0x3000000
+    args = lambda **kw: {**dict(tokens=4, qh=2, kh=1, hd=128, eps=1e-6, dims=128, trad=0,
+                                base=10000.0, scale=1.0, offset=0, freqs=None, dt=BF16), **kw}
+
+    def call(**kw):
+        a = args(**kw)
+        return lib.fnorm_dual_head_rms_rope(A, B, C, D, E, F, a["tokens"], a["qh"], a["kh"],
+                                            a["hd"], a["eps"], a["dims"], a["trad"], a["base"],
+                                            a["scale"], a["offset"], a["freqs"], a["dt"], None)
+    assert call(dims=127) == 2
+    assert call(dims=0) == 2
+    assert call(dims=130) == 2
+    assert call(base=0.0) == 2
+    assert call(base=float("nan")) == 2
+    assert call(scale=float("inf")) == 2
+    assert call(offset=-1) == 2
+    assert call(tokens=-1) == 2
+    assert call(qh=-2) == 2
+    assert call(eps=-1.0) == 3
+    assert call(dt=5) == 4
+    assert call(tokens=0) == 0
+    assert lib.fnorm_last_error() == b""
+    # head shapes the kernel cannot serve are refused, not run
+    assert trn.rope_variant_count(BF16, 1024, 128, False) == 0
+    assert trn.rope_variant_count(BF16, 128, 128, False) >= 2
+    assert trn.rope_variant_count(BF16, 128, 128, True) >= 2
+    assert "lpr16" in trn.describe_rope(BF16, 128, 128, False)
+    assert trn.rope_variant_count(BF16, 128, 127, False) == 0

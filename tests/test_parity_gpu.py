@@ -397,3 +397,85 @@ def test_composed_iota_page_case(o):
     torch.cuda.synchronize()
     assert float((yc - yf).abs().max()) <= 1e-5
     helpers.check("rms", yc.cpu(), run_oracle(o, "rms", wl.tensors, wl.eps), label="composed iota")
+
+
+# ----------------------------------------------------------------- dual norm + RoPE
+def rope_floor(w: torch.Tensor, dims: int, traditional: bool) -> np.ndarray:
+    """Error floor per feature: max(|w_a|, |w_b|) over the rotated pair."""
+    wd = np.abs(helpers.widen(w))
+    f = wd.copy()
+    half = dims // 2
+    for i in range(half):
+        a, b = (2 * i, 2 * i + 1) if traditional else (i, i + half)
+        m = max(wd[a], wd[b])
+        f[a] = f[b] = m
+    return f
+
+
+ROPE_CASES = [  # (dtype, tokens, q_heads, k_heads, head_dim, dims, traditional, base, scale, offset, table)
+    (torch.bfloat16, 200, 32, 8, 128, 128, False, 10000.0, 1.0, 0, False),
+    (torch.bfloat16, 200, 32, 8, 128, 128, True, 10000.0, 1.0, 4000, False),
+    (torch.float32, 97, 4, 2, 128, 128, False, 500000.0, 1.0, 131072, False),
+    (torch.float32, 97, 4, 2, 128, 64, True, 10000.0, 0.5, 7, False),
+    (torch.bfloat16, 64, 16, 4, 64, 64, False, 10000.0, 1.0, 100, True),
+    (torch.bfloat16, 33, 8, 8, 256, 256, False, 1000000.0, 1.0, 3, False),
+    (torch.bfloat16, 33, 8, 2, 256, 32, False, 10000.0, 1.0, 3, False),
+    (torch.bfloat16, 50, 6, 2, 96, 96, False, 10000.0, 1.0, 11, False),
+    (torch.float32, 50, 6, 2, 80, 80, True, 10000.0, 2.0, 11, True),
+    (torch.bfloat16, 21, 3, 1, 100, 100, True, 10000.0, 1.0, 5, False),
+    (torch.float32, 17, 2, 1, 1024, 1024, False, 10000.0, 1.0, 12345, False),
+    (torch.bfloat16, 1, 1, 0, 128, 128, False, 10000.0, 1.0, 9, False),
+    (torch.bfloat16, 5, 0, 4, 128, 128, True, 10000.0, 1.0, 9, False),
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES, ids=lambda c: f"{str(c[0])[6:]}-t{c[1]}-h{c[2]}/{c[3]}-hd{c[4]}-d{c[5]}-{'il' if c[6] else 'sh'}-o{c[9]}{'-tab' if c[10] else ''}")
+def test_dual_rope_matches_oracle(o, case):
+    dtype, tokens, qh, kh, hd, dims, trad, base, scale, offset, table = case
+    g = torch.Generator().manual_seed(hd * 7 + dims)
+    q = torch.randn(tokens, qh, hd, generator=g).to(dtype)
+    k = torch.randn(tokens, kh, hd, generator=g).to(dtype)
+    qw = (1 + 0.1 * torch.randn(hd, generator=g)).to(dtype)
+    kw = (1 + 0.1 * torch.randn(hd, generator=g)).to(dtype)
+    freqs = None
+    if table:
+        freqs = (base ** (-torch.arange(0, dims, 2, dtype=torch.float64) / dims)
+                 * (1 + 0.3 * torch.rand(dims // 2, generator=g, dtype=torch.float64))).float()
+    code = trn.F32 if dtype == torch.float32 else trn.BF16
+    n = trn.rope_variant_count(code, hd, dims, trad)
+    assert n >= 2
+    rq, rk = o.dual_head_rms_rope(helpers.to_oracle_array(q), helpers.to_oracle_array(k),
+                                  helpers.to_oracle_array(qw), helpers.to_oracle_array(kw),
+                                  1e-6, dims, trad, base, scale, offset,
+                                  None if freqs is None else freqs.numpy())
+    fq, fk = rope_floor(qw, dims, trad), rope_floor(kw, dims, trad)
+    dq, dk, dqw, dkw = (t.to(DEV) for t in (q, k, qw, kw))
+    dfr = None if freqs is None else freqs.to(DEV)
+    plain_q, plain_k = trn.dual_head_rms_norm(dq, dk, dqw, dkw, 1e-6)
+    for v in range(n):
+        say(f"[rope] {case} v={v} {trn.describe_rope(code, hd, dims, trad, variant=v)}")
+        yq, yk = trn.dual_head_rms_rope(dq, dk, dqw, dkw, 1e-6, dims=dims, traditional=trad,
+                                        base=base, scale=scale, offset=offset, freqs=dfr,
+                                        variant=v)
+        torch.cuda.synchronize()
+        if qh:
+            helpers.check("rms", yq.cpu(), rq, label=f"rope q v{v}", floor=fq)
+        if kh:
+            helpers.check("rms", yk.cpu(), rk, label=f"rope k v{v}", floor=fk)
+        if offset == 0 and tokens > 0:
+            # token 0 sits at position 0: bitwise the plain dual norm
+            assert torch.equal(yq[0].cpu().view(torch.uint8), plain_q[0].cpu().view(torch.uint8))
+            assert torch.equal(yk[0].cpu().view(torch.uint8), plain_k[0].cpu().view(torch.uint8))
+
+
+def test_dual_rope_full_size(o):
+    """The dual workload's full shape with RoPE (positions 0..4095)."""
+    wl = inputs.dual_bf16_4096tok()
+    t = wl.tensors
+    q, k, qw, kw = (t[n].to(DEV) for n in ("q", "k", "qw", "kw"))
+    yq, yk = trn.dual_head_rms_rope(q, k, qw, kw, wl.eps)
+    torch.cuda.synchronize()
+    rq, rk = o.dual_head_rms_rope(*(helpers.to_oracle_array(t[n]) for n in ("q", "k", "qw", "kw")),
+                                  wl.eps, 128, False, 10000.0, 1.0, 0)
+    helpers.check("rms", yq.cpu(), rq, label="rope full q", floor=rope_floor(t["qw"], 128, False))
+    helpers.check("rms", yk.cpu(), rk, label="rope full k", floor=rope_floor(t["kw"], 128, False))

@@ -55,6 +55,12 @@ _SIGNATURES = {
     "fnorm_version": ([], _I),
     "fnorm_bench_copy": ([_P, _P, _I64, _P], _I),
     "fnorm_composed_workspace_bytes": ([_I, _I64, _I64], _I64),
+    "fnorm_dual_head_rms_rope": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _I64, _I,
+                                  _F, _F, _I64, _P, _I, _P], _I),
+    "fnorm_dual_head_rms_rope_v": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _I64, _I,
+                                    _F, _F, _I64, _P, _I, _P, _I], _I),
+    "fnorm_rope_variant_count": ([_I, _I64, _I64, _I, _I], _I),
+    "fnorm_describe_rope": ([_I, _I64, _I64, _I, _I, _I, ctypes.c_char_p, _I64], _I),
     "fnorm_rms_composed": ([_P, _P, _P, _I64, _I64, _F, _I, _P, _I64, _P], _I),
     "fnorm_layer_composed": ([_P, _P, _P, _P, _I64, _I64, _F, _I, _P, _I64, _P], _I),
 }
@@ -235,6 +241,55 @@ def layer_norm_composed(x, w, b=None, eps: float = 1e-5, out=None, workspace=Non
                                       width, eps, code, _ptr(ws), ws.numel() * ws.element_size(),
                                       _stream(x)))
     return y
+
+
+def dual_head_rms_rope(q, k, qw, kw, eps: float = 1e-6, dims: int | None = None,
+                       traditional: bool = False, base: float = 10000.0, scale: float = 1.0,
+                       offset: int = 0, freqs=None, q_out=None, k_out=None, variant: int = -1):
+    """One launch: RoPE(RMSNorm(q, qw)) and RoPE(RMSNorm(k, kw)).
+    q [tokens, q_heads, head_dim], k [tokens, k_heads, head_dim]; dims
+    (default head_dim) features rotate, split-half pairs unless
+    `traditional`; freqs: optional float32 GPU tensor of dims/2 inverse
+    frequencies replacing the base schedule; offset: position of token 0."""
+    torch = _torch()
+    if not q.is_cuda:
+        raise ValueError("q must be a GPU tensor")
+    code = _dtype_code(q)
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise ValueError("q [tokens, q_heads, hd] and k [tokens, k_heads, hd] expected")
+    tokens, qh, hd = q.shape
+    kh = k.shape[1]
+    for t, n in ((q, "q"), (k, "k"), (qw, "qw"), (kw, "kw")):
+        _require(t, n, q.dtype, q.device)
+    if tuple(qw.shape) != (hd,) or tuple(kw.shape) != (hd,):
+        raise ValueError("qw and kw must have shape (head_dim,)")
+    dims = hd if dims is None else dims
+    if freqs is not None:
+        _require(freqs, "freqs", torch.float32, q.device)
+        if tuple(freqs.shape) != (dims // 2,):
+            raise ValueError("freqs must have dims/2 entries")
+    qy = torch.empty_like(q) if q_out is None else q_out
+    ky = torch.empty_like(k) if k_out is None else k_out
+    _require(qy, "q_out", q.dtype, q.device)
+    _require(ky, "k_out", q.dtype, q.device)
+    _check(lib().fnorm_dual_head_rms_rope_v(
+        _ptr(q), _ptr(k), _ptr(qw), _ptr(kw), _ptr(qy), _ptr(ky), tokens, qh, kh, hd, eps, dims,
+        1 if traditional else 0, base, scale, offset, _ptr(freqs), code, _stream(q), variant))
+    return qy, ky
+
+
+def rope_variant_count(dtype_code: int, head_dim: int, dims: int, traditional: bool,
+                       aligned: bool = True) -> int:
+    return lib().fnorm_rope_variant_count(dtype_code, head_dim, dims, int(traditional),
+                                          int(aligned))
+
+
+def describe_rope(dtype_code: int, head_dim: int, dims: int, traditional: bool,
+                  aligned: bool = True, variant: int = -1) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().fnorm_describe_rope(dtype_code, head_dim, dims, int(traditional), int(aligned),
+                                     variant, buf, 256))
+    return buf.value.decode()
 
 
 def variant_count(op: int, dtype_code: int, width: int, aligned: bool = True) -> int:

@@ -52,6 +52,7 @@ const Registry& registry() {
         Registry reg;
         register_f32(reg.table);
         register_bf16(reg.table);
+        register_rope(reg.table);
         reg.occupancy.reset(new std::atomic<int>[reg.table.size()]);
         for (size_t i = 0; i < reg.table.size(); ++i) reg.occupancy[i].store(0);
         return reg;
@@ -101,10 +102,59 @@ int candidates(int kind, int dt, int64_t width, bool aligned, const Variant** ou
         if (const Variant* m = smallest_masked(kind, dt, vec, width)) out[n++] = m;
     }
     if (const Variant* s = smallest_masked(kind, dt, 1, width)) out[n++] = s;
-    if (kind != K_DUAL) {
+    if (kind == K_RMS || kind == K_LAYER || kind == K_LAYER_NOBIAS) {
         if (vec_ok)
             if (const Variant* w = find_wide(kind, dt, vec)) out[n++] = w;
         if (const Variant* w = find_wide(kind, dt, 1)) out[n++] = w;
+    }
+    return n;
+}
+
+// Whether a fused RoPE kernel shape can reach the pair partners of a
+// rotation over the first `dims` features (see dual_rope_rows).
+bool rope_ok(const Variant& v, int64_t dims) {
+    if (v.kind == K_ROPE_TRAD) return v.vec >= 2 || v.lpr >= 2;
+    const int64_t half = dims / 2;
+    if (half % v.vec != 0) return false;
+    const int64_t dp = half / v.vec;
+    if (v.vpt == 1) return 2 * dp <= v.lpr;
+    return dp % v.lpr == 0;
+}
+
+// LDS bytes of a fused RoPE launch: inverse frequencies (fp64) plus one
+// (cos, sin) fp32 table per row slot.
+int64_t rope_lds_bytes(const Variant& v, int64_t dims) {
+    const int64_t half = dims / 2;
+    return half * 8 + int64_t(v.rows_per_block()) * half * 8;
+}
+
+constexpr int64_t kMaxLds = 64 * 1024;
+
+// Fused RoPE kernels able to serve the request, default first: exact
+// shapes, the smallest masked 16-byte-pack shape, the smallest masked
+// scalar shape; each only if it reaches the partners and fits in LDS.
+int rope_candidates(int kind, int dt, int64_t width, bool aligned, int64_t dims,
+                    const Variant** out) {
+    int n = 0;
+    const int vec = 16 / elem_bytes(dt);
+    const bool vec_ok = aligned && (width % vec == 0);
+    auto usable = [&](const Variant& v) {
+        return v.kind == kind && v.dt == dt && rope_ok(v, dims) &&
+               rope_lds_bytes(v, dims) <= kMaxLds && v.capacity() >= width;
+    };
+    if (vec_ok)
+        for (const Variant& v : registry().table)
+            if (usable(v) && v.vec == vec && !v.masked && v.capacity() == width &&
+                n < kMaxCandidates - 2)
+                out[n++] = &v;
+    for (int pass_vec : {vec_ok ? vec : 0, 1}) {
+        if (pass_vec == 0) continue;
+        const Variant* best = nullptr;
+        for (const Variant& v : registry().table)
+            if (usable(v) && v.vec == pass_vec && v.masked &&
+                (!best || v.capacity() < best->capacity()))
+                best = &v;
+        if (best) out[n++] = best;
     }
     return n;
 }
@@ -130,7 +180,7 @@ void describe_choice(const Choice& c, char* buf, size_t len) {
     const Variant& v = *c.v;
     static const char* nts[] = {"", ".ntst", ".ntld", ".nt"};
     const char* nt = nts[(v.nt & NT_LOAD ? 2 : 0) | (v.nt & NT_STORE ? 1 : 0)];
-    static const char* kinds[] = {"rms", "layer", "layer", "dual", "copy"};
+    static const char* kinds[] = {"rms", "layer", "layer", "dual", "copy", "ropesplit", "ropeinter"};
     if (v.wide)
         std::snprintf(buf, len, "%s.%s.vec%d.wide.blk%d.%s", kinds[v.kind], dtype_name(v.dt),
                       v.vec, v.block, c.persistent ? "persistent" : "grid");
@@ -319,6 +369,92 @@ int fnorm_dual_head_rms(const void* q, const void* k, const void* qw, const void
                                  stream, -1);
 }
 
+int fnorm_dual_head_rms_rope_v(const void* q, const void* k, const void* qw, const void* kw,
+                               void* qy, void* ky, int64_t tokens, int64_t q_heads,
+                               int64_t k_heads, int64_t head_dim, float eps, int64_t rope_dims,
+                               int traditional, float base, float scale, int64_t offset,
+                               const float* freqs, int dtype, void* stream, int variant) {
+    static const char* op = "fnorm_dual_head_rms_rope";
+    if (tokens < 0 || q_heads < 0 || k_heads < 0)
+        return fail(FNORM_ERR_SHAPE, op, "tokens=%lld q_heads=%lld k_heads=%lld must be >= 0",
+                    (long long)tokens, (long long)q_heads, (long long)k_heads);
+    if (q_heads > (int64_t(1) << 30) || k_heads > (int64_t(1) << 30) ||
+        (tokens > 0 && (q_heads + k_heads) > (INT64_MAX / 16) / tokens))
+        return fail(FNORM_ERR_SHAPE, op, "tokens * heads overflows");
+    const int64_t q_rows = tokens * q_heads, k_rows = tokens * k_heads;
+    if (int s = check_scalars(op, dtype, q_rows + k_rows, head_dim, eps)) return s;
+    if (rope_dims < 2 || rope_dims % 2 != 0 || rope_dims > head_dim)
+        return fail(FNORM_ERR_SHAPE, op, "rope_dims=%lld must be even and in [2, head_dim=%lld]",
+                    (long long)rope_dims, (long long)head_dim);
+    if (!std::isfinite(scale) || (!freqs && (!std::isfinite(base) || base <= 0.0f)))
+        return fail(FNORM_ERR_SHAPE, op, "base must be finite and > 0, scale finite");
+    if (offset < 0 || offset > (int64_t(1) << 52) - tokens)
+        return fail(FNORM_ERR_SHAPE, op, "offset=%lld out of range", (long long)offset);
+    if (q_rows + k_rows == 0) return ok();
+    if (q_rows > 0 && (!q || !qw || !qy))
+        return fail(FNORM_ERR_NULL, op, "q, qw and qy must be non-NULL when q rows exist");
+    if (k_rows > 0 && (!k || !kw || !ky))
+        return fail(FNORM_ERR_NULL, op, "k, kw and ky must be non-NULL when k rows exist");
+    const int64_t eb = elem_bytes(dtype);
+    const int64_t qb = q_rows * head_dim * eb, kb = k_rows * head_dim * eb, wb = head_dim * eb;
+    if (qy != q && overlap(qy, qb, q, qb)) return fail(FNORM_ERR_ALIAS, op, "qy overlaps q");
+    if (ky != k && overlap(ky, kb, k, kb)) return fail(FNORM_ERR_ALIAS, op, "ky overlaps k");
+    if (overlap(qy, qb, k, kb) || overlap(ky, kb, q, qb) || overlap(qy, qb, ky, kb))
+        return fail(FNORM_ERR_ALIAS, op, "an output overlaps another tensor");
+    if (overlap(qy, qb, qw, q_rows > 0 ? wb : 0) || overlap(qy, qb, kw, k_rows > 0 ? wb : 0) ||
+        overlap(ky, kb, qw, q_rows > 0 ? wb : 0) || overlap(ky, kb, kw, k_rows > 0 ? wb : 0) ||
+        overlap(qy, qb, freqs, rope_dims * 2) || overlap(ky, kb, freqs, rope_dims * 2))
+        return fail(FNORM_ERR_ALIAS, op, "an output overlaps a weight or the frequency table");
+    const bool al = (q_rows == 0 || (aligned16(q) && aligned16(qw) && aligned16(qy))) &&
+                    (k_rows == 0 || (aligned16(k) && aligned16(kw) && aligned16(ky)));
+    const int kind = traditional ? K_ROPE_TRAD : K_ROPE_SPLIT;
+    const Variant* list[kMaxCandidates];
+    const int n = rope_candidates(kind, dtype, head_dim, al, rope_dims, list);
+    if (variant < 0) variant = 0;
+    if (variant >= 2 * n)
+        return fail(FNORM_ERR_UNSUPPORTED, op,
+                    "no fused kernel for head_dim %lld, rope_dims %lld (variant %d)",
+                    (long long)head_dim, (long long)rope_dims, variant);
+    const Variant* v = list[variant / 2];
+    const bool persistent = variant % 2 == 0;
+    const void* qw_eff = q_rows > 0 ? qw : kw;
+    const void* kw_eff = k_rows > 0 ? kw : qw;
+    RopeArgs ra{NormArgs{q, qw_eff, nullptr, qy, k, kw_eff, ky, q_rows + k_rows, q_rows, head_dim,
+                         eps},
+                q_heads > 0 ? q_heads : 1, k_heads > 0 ? k_heads : 1, rope_dims, offset, base,
+                scale, freqs};
+    const int64_t lds = rope_lds_bytes(*v, rope_dims);
+    const int64_t rpb = v->rows_per_block();
+    int64_t grid = (ra.n.rows + rpb - 1) / rpb;
+    if (persistent) {
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, v->fn, v->block, size_t(lds)) !=
+                hipSuccess || per_cu <= 0)
+            per_cu = 1;
+        const int64_t cap = int64_t(device_cus()) * per_cu;
+        if (grid > cap) grid = cap;
+    }
+    if (grid > (int64_t(1) << 30)) grid = int64_t(1) << 30;
+    void* args[] = {&ra};
+    hipError_t e = hipLaunchKernel(v->fn, dim3(unsigned(grid)), dim3(unsigned(v->block)), args,
+                                   size_t(lds), static_cast<hipStream_t>(stream));
+    hipError_t e2 = hipGetLastError();
+    if (e == hipSuccess) e = e2;
+    if (e != hipSuccess)
+        return fail(FNORM_ERR_LAUNCH, op, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int fnorm_dual_head_rms_rope(const void* q, const void* k, const void* qw, const void* kw,
+                             void* qy, void* ky, int64_t tokens, int64_t q_heads,
+                             int64_t k_heads, int64_t head_dim, float eps, int64_t rope_dims,
+                             int traditional, float base, float scale, int64_t offset,
+                             const float* freqs, int dtype, void* stream) {
+    return fnorm_dual_head_rms_rope_v(q, k, qw, kw, qy, ky, tokens, q_heads, k_heads, head_dim,
+                                      eps, rope_dims, traditional, base, scale, offset, freqs,
+                                      dtype, stream, -1);
+}
+
 int fnorm_variant_count(int op, int dtype, int64_t width, int aligned) {
     if ((dtype != FNORM_F32 && dtype != FNORM_BF16) || width <= 0 || op < 0 || op > 2) return 0;
     const Variant* list[kMaxCandidates];
@@ -337,6 +473,34 @@ int fnorm_describe(int op, int dtype, int64_t width, int aligned, int variant, c
     Choice c;
     if (!pick(op_kind(op, true), dtype, width, aligned != 0, variant, &c))
         return fail(FNORM_ERR_UNSUPPORTED, name, "no variant %d", variant);
+    describe_choice(c, buf, size_t(len));
+    return ok();
+}
+
+int fnorm_rope_variant_count(int dtype, int64_t head_dim, int64_t rope_dims, int traditional,
+                             int aligned) {
+    if ((dtype != FNORM_F32 && dtype != FNORM_BF16) || head_dim <= 0 || rope_dims < 2 ||
+        rope_dims % 2 != 0 || rope_dims > head_dim)
+        return 0;
+    const Variant* list[kMaxCandidates];
+    return 2 * rope_candidates(traditional ? K_ROPE_TRAD : K_ROPE_SPLIT, dtype, head_dim,
+                               aligned != 0, rope_dims, list);
+}
+
+int fnorm_describe_rope(int dtype, int64_t head_dim, int64_t rope_dims, int traditional,
+                        int aligned, int variant, char* buf, int64_t len) {
+    static const char* name = "fnorm_describe_rope";
+    if (!buf || len <= 0) return fail(FNORM_ERR_NULL, name, "buf must be non-NULL, len > 0");
+    buf[0] = '\0';
+    const int n = fnorm_rope_variant_count(dtype, head_dim, rope_dims, traditional, aligned);
+    if (variant < 0) variant = 0;
+    if (variant >= n) return fail(FNORM_ERR_UNSUPPORTED, name, "no variant %d", variant);
+    const Variant* list[kMaxCandidates];
+    rope_candidates(traditional ? K_ROPE_TRAD : K_ROPE_SPLIT, dtype, head_dim, aligned != 0,
+                    rope_dims, list);
+    Choice c;
+    c.v = list[variant / 2];
+    c.persistent = variant % 2 == 0;
     describe_choice(c, buf, size_t(len));
     return ok();
 }

@@ -132,6 +132,34 @@ constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <- lane 7 - i within 8
 constexpr int DPP_ROW_MIRROR = 0x140;       // lane i <- lane 15 - i within 16
 constexpr int SWIZZLE_XOR16 = 0x401F;       // bitmask mode: and 0x1f, xor 0x10
 
+// DPP row shifts / rotation (within 16-lane rows).
+constexpr int DPP_ROW_SHL4 = 0x104;   // lane l <- lane l + 4
+constexpr int DPP_ROW_SHR4 = 0x114;   // lane l <- lane l - 4
+constexpr int DPP_ROW_ROR8 = 0x128;   // lane l <- lane l ^ 8 (rotate by 8 of 16)
+
+// The value held by lane (l ^ d) of the wavefront, for a pair distance d
+// that is a power of two, through the cheapest path: DPP for d <= 8,
+// ds_swizzle for d = 16, ds_bpermute otherwise (also for d not a power of
+// two, where `bperm_addr` names the source lane * 4).
+__device__ __forceinline__ float lane_partner(float v, int d, int wave_lane, int bperm_addr) {
+    switch (d) {
+        case 1: return dpp<DPP_QUAD_1032>(v);
+        case 2: return dpp<DPP_QUAD_2301>(v);
+        case 4: {
+            const float up = dpp<DPP_ROW_SHL4>(v);
+            const float down = dpp<DPP_ROW_SHR4>(v);
+            return (wave_lane & 4) ? down : up;
+        }
+        case 8: return dpp<DPP_ROW_ROR8>(v);
+        case 16:
+            return __builtin_bit_cast(
+                float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), SWIZZLE_XOR16));
+        default:
+            return __builtin_bit_cast(
+                float, __builtin_amdgcn_ds_bpermute(bperm_addr, __builtin_bit_cast(int, v)));
+    }
+}
+
 // Sum over aligned groups of G consecutive lanes (G a power of two <= 64).
 // Each step adds a value that is already uniform over the partner half, so
 // the result is bitwise identical in every lane of the group.

@@ -304,3 +304,264 @@ __global__ __launch_bounds__(BLOCK) void copy16(const u32x4* __restrict__ src,
 }
 
 }  // namespace fnorm
+
+namespace fnorm {
+
+// ---------------------------------------------------------------------------
+// Dual q/k head RMSNorm fused with the rotary position embedding (RoPE) of
+// both outputs, one launch.  Norm definition as above; RoPE (Emily.Fast
+// docs, `rope` and `rope_with_freqs`): pair i of a head vector at position
+// p = offset + token rotates by theta_i = p * scale * inv_freq_i, with
+// inv_freq_i = base^(-2i/dims) or a given table; pairs are (i, i + dims/2)
+// (split-half) or (2i, 2i + 1) (TRAD, interleaved); features past `dims`
+// pass through.  The result is RoPE(RMSNorm(x)) rounded once.
+//
+// Rows are head vectors in [token][head] order, so the heads of one token
+// are consecutive rows.  Each wavefront evaluates the (cos, sin) table once
+// per token among its rows (the first slot of each token, found with one
+// ballot) into its own LDS region, and every row of that token reads it;
+// the table is private to the wavefront, so no workgroup barrier is needed
+// in the row loop.  The angle in turns, theta / (2 pi), is formed
+// in fp64 and reduced exactly to its fractional part f in [-1/2, 1/2]; sin
+// and cos of 2 pi f then come from the hardware v_sin_f32 / v_cos_f32 (which
+// take turns), so large positions keep fp32-level accuracy at the cost of a
+// few instructions.
+// Split-half partners live in another lane (fetched with ds_bpermute, the
+// pack layout puts pack p + dims/(2 VEC) in lane p + dims/(2 VEC) when a
+// thread holds one pack) or in the same thread (when dims/(2 VEC) is a
+// multiple of LPR); interleaved partners sit in the same 16-byte pack (in the
+// neighbouring lane for scalar packs).  The host only launches shapes for
+// which one of these holds.
+struct RopeArgs {
+    NormArgs n;          // x = q, w = qw, y = qy, x2 = k, w2 = kw, y2 = ky
+    int64_t q_heads;     // >= 1 (1 when there are no query rows)
+    int64_t k_heads;     // >= 1 (1 when there are no key rows)
+    int64_t dims;        // rotated features, even, <= width
+    int64_t offset;      // position of token 0
+    float base;
+    float scale;
+    const float* freqs;  // dims/2 inverse frequencies, or null
+};
+
+template <int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, int NT, bool TRAD>
+__global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
+    using R = typename Raw<DT, VEC>::type;
+    static_assert(LPR <= 64 && BLOCK % 64 == 0 && BLOCK % LPR == 0, "launch shape");
+    constexpr int RPB = BLOCK / LPR;
+    constexpr bool NT_LD = (NT & NT_LOAD) != 0;
+    constexpr bool NT_ST = (NT & NT_STORE) != 0;
+    extern __shared__ double rope_smem[];   // inv_freq[half], then (cos, sin)[RPB][half]
+
+    const NormArgs& a = ra.n;
+    const int tid = threadIdx.x;
+    const int group = tid / LPR;
+    const int lane = tid % LPR;
+    const int wave_lane = tid & 63;
+    const int64_t width = a.width;
+    const float fwidth = static_cast<float>(width);
+    const int64_t last = a.rows - 1;
+    const int64_t half = ra.dims / 2;
+    double* invf = rope_smem;
+    float2* cs = reinterpret_cast<float2*>(rope_smem + half);
+
+    // inverse frequencies in turns per position: inv_freq_i / (2 pi), fp64
+    constexpr double kInvTwoPi = 0.15915494309189533577;
+    for (int64_t i = tid; i < half; i += BLOCK)
+        invf[i] = kInvTwoPi *
+                  (ra.freqs ? static_cast<double>(ra.freqs[i])
+                            : pow(static_cast<double>(ra.base),
+                                  -2.0 * static_cast<double>(i) / static_cast<double>(ra.dims)));
+
+    auto col_of = [&](int v) { return int64_t(v * LPR + lane) * VEC; };
+    auto in_row = [&](int v) { return !MASKED || col_of(v) < width; };
+    constexpr int W = 64 / LPR;                 // rows per wavefront
+    const int wave = tid >> 6;
+    const int wslot = wave_lane / LPR;          // this row's slot in the wave
+    float2* wtab = cs + int64_t(wave) * W * half;
+    const int ihalf = static_cast<int>(half);
+
+    R wv[VPT], wv2[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        wv[v] = in_row(v) ? load_raw<DT, VEC, false>(a.w, col_of(v)) : raw_zero<DT, VEC>();
+        wv2[v] = in_row(v) ? load_raw<DT, VEC, false>(a.w2, col_of(v)) : raw_zero<DT, VEC>();
+    }
+    __syncthreads();   // inverse frequencies ready; no workgroup barrier after this
+
+    const bool small = a.rows <= 0x7fffffff;
+    for (int64_t base = int64_t(blockIdx.x) * RPB; base < a.rows;
+         base += int64_t(gridDim.x) * RPB) {
+        // This row's loads are issued first, so their latency overlaps the
+        // angle-table phase below.
+        const bool valid = base + group <= last;
+        const int64_t row = valid ? base + group : last;
+        const bool second = row >= a.rows1;
+        const void* xp = second ? a.x2 : a.x;
+        void* yp = second ? a.y2 : a.y;
+        const int64_t row_off = (second ? row - a.rows1 : row) * width;
+        R xv[VPT];
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+            xv[v] = in_row(v) ? load_raw<DT, VEC, NT_LD>(xp, row_off + col_of(v))
+                              : raw_zero<DT, VEC>();
+
+        // Token of this row, its position, and the first slot of this
+        // wavefront holding the same token (the slot that owns the table).
+        const int64_t num = second ? row - a.rows1 : row;
+        const int64_t den = second ? ra.k_heads : ra.q_heads;
+        const int64_t tok = small ? int64_t(uint32_t(num) / uint32_t(den)) : num / den;
+        const int64_t first = (second ? a.rows1 : 0) + tok * den;
+        const int64_t wave_row0 = base + int64_t(wave) * W;
+        const int leader = first > wave_row0 ? int(first - wave_row0) : 0;
+        const double pos = static_cast<double>(ra.offset + tok) * static_cast<double>(ra.scale);
+
+        // Angle table of the wavefront's leader slots: leader k's pair i is
+        // work item k * half + i, spread round-robin over the 64 lanes.
+        uint64_t leaders = __ballot(lane == 0 && leader == wslot);
+        int k = 0;
+        while (leaders) {                                   // uniform over the wave
+            const int bit = __builtin_ctzll(leaders);
+            leaders &= leaders - 1;
+            const int g = bit / LPR;
+            const int64_t pb = __builtin_bit_cast(int64_t, pos);
+            const int lo = __builtin_amdgcn_readlane(int(pb & 0xffffffff), bit);
+            const int hi = __builtin_amdgcn_readlane(int(pb >> 32), bit);
+            const double pg = __builtin_bit_cast(double, (int64_t(hi) << 32) | uint32_t(lo));
+            for (int i = (wave_lane - (k * ihalf) % 64 + 64) % 64; i < ihalf; i += 64) {
+                // theta / (2 pi) in fp64, reduced to a fraction of a turn
+                // exactly (t - rint(t)); the hardware sine and cosine take
+                // their argument in turns (v_sin_f32 / v_cos_f32)
+                const double t = pg * invf[i];
+                const float f = static_cast<float>(t - __builtin_rint(t));
+                wtab[g * ihalf + i] =
+                    make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+            }
+            ++k;
+        }
+        // the table is written and read by this wavefront only
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        const float2* tab = wtab + leader * ihalf;
+        // Split-half, one pack per thread: this lane's (cos, sin) entries are
+        // read now, while the row's loads are still in flight.
+        const int64_t dp = half / VEC;     // partner distance in packs
+        float2 tpre[(!TRAD && VPT == 1) ? VEC : 1];
+        if constexpr (!TRAD && VPT == 1) {
+            const int64_t p = lane;
+            const int64_t t0 = p < 2 * dp ? (p < dp ? p : p - dp) * VEC : 0;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) tpre[i] = tab[t0 + i];
+        }
+
+        float ss = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                const float f = elem<DT, VEC>(xv[v], i);
+                ss = __builtin_fmaf(f, f, ss);
+            }
+        ss = lane_group_sum<LPR>(ss);
+        const float scale = __builtin_amdgcn_rsqf(ss / fwidth + a.eps);
+
+        float o[VPT][VEC];
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const R wr = second ? wv2[v] : wv[v];
+#pragma unroll
+            for (int i = 0; i < VEC; ++i)
+                o[v][i] = (elem<DT, VEC>(xv[v], i) * scale) * elem<DT, VEC>(wr, i);
+        }
+
+        // rotation of the normalized values
+        float out[VPT][VEC];
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) out[v][i] = o[v][i];
+        if constexpr (TRAD) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                if constexpr (VEC >= 2) {
+#pragma unroll
+                    for (int i = 0; i < VEC; i += 2) {
+                        const int64_t c = col_of(v) + i;
+                        if (c < ra.dims) {
+                            const float2 t = tab[c / 2];
+                            out[v][i] = o[v][i] * t.x - o[v][i + 1] * t.y;
+                            out[v][i + 1] = o[v][i + 1] * t.x + o[v][i] * t.y;
+                        }
+                    }
+                } else {
+                    // scalar packs: the pair partner is the neighbouring lane
+                    const int src = (wave_lane ^ 1) << 2;
+                    const float p = __builtin_bit_cast(
+                        float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, o[v][0])));
+                    const int64_t c = col_of(v);
+                    if (c < ra.dims) {
+                        const float2 t = tab[c / 2];
+                        out[v][0] = (c & 1) ? o[v][0] * t.x + p * t.y : o[v][0] * t.x - p * t.y;
+                    }
+                }
+            }
+        } else {
+            if constexpr (VPT == 1) {
+                // one pack per thread: the partner pack is in lane lane +- dp.
+                // All partner values and table entries are fetched before
+                // any is used, so the LDS operations overlap.
+                const int64_t p = lane;
+                const bool rot = p < 2 * dp;
+                const int64_t partner = p < dp ? p + dp : (rot ? p - dp : p);
+                const int src = (wave_lane - lane + int(partner)) << 2;
+                // power-of-two distances: the partner is lane ^ dp (DPP or
+                // swizzle, no LDS traffic); others go through ds_bpermute
+                const int d = (dp & (dp - 1)) == 0 ? int(dp) : 0;
+                float q[VEC];
+                const float2* t = tpre;
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) q[i] = lane_partner(o[0][i], d, wave_lane, src);
+                if (rot) {
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i)
+                        out[0][i] = p < dp ? o[0][i] * t[i].x - q[i] * t[i].y
+                                           : o[0][i] * t[i].x + q[i] * t[i].y;
+                }
+            } else {
+                // the partner pack is in this thread, dp / LPR packs away
+                // (the host launches VPT > 1 only when dp % LPR == 0)
+                const int dv = int(dp / LPR);
+#pragma unroll
+                for (int v = 0; v < VPT; ++v) {
+                    const int64_t p = int64_t(v) * LPR + lane;
+                    if (p < 2 * dp) {
+                        const bool first = p < dp;
+                        const int vp = first ? v + dv : v - dv;
+#pragma unroll
+                        for (int i = 0; i < VEC; ++i) {
+                            float q = 0.0f;
+#pragma unroll
+                            for (int u = 0; u < VPT; ++u)
+                                if (u == vp) q = o[u][i];
+                            const float2 t = tab[(first ? p : p - dp) * VEC + i];
+                            out[v][i] = first ? o[v][i] * t.x - q * t.y : o[v][i] * t.x + q * t.y;
+                        }
+                    }
+                }
+            }
+        }
+
+        if (valid) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v)
+                if (in_row(v))
+                    store_raw<DT, VEC, NT_ST>(yp, row_off + col_of(v), make_raw<DT, VEC>(out[v]));
+        }
+        // every lane has read the table before the next block-row rewrites it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+}
+
+}  // namespace fnorm

@@ -13,7 +13,10 @@
 
 namespace fnorm {
 
-enum Kind : int { K_RMS = 0, K_LAYER = 1, K_LAYER_NOBIAS = 2, K_DUAL = 3, K_COPY = 4 };
+enum Kind : int {
+    K_RMS = 0, K_LAYER = 1, K_LAYER_NOBIAS = 2, K_DUAL = 3, K_COPY = 4,
+    K_ROPE_SPLIT = 5, K_ROPE_TRAD = 6   // dual head RMSNorm + RoPE (split-half / interleaved)
+};
 
 struct Variant {
     const void* fn;     // host stub of the __global__ function
@@ -35,5 +38,7 @@ struct Variant {
 // instance of that element type, in preference order.
 void register_f32(std::vector<Variant>& table);
 void register_bf16(std::vector<Variant>& table);
+// Defined in fnorm_inst_rope.hip: the fused dual norm + RoPE instances.
+void register_rope(std::vector<Variant>& table);
 
 }  // namespace fnorm
