@@ -10,8 +10,9 @@ RMSNorm, all in IEEE double).  This module compiles it with gcc and exposes
 it through ctypes.  ``exact_tiny`` holds an exact-rational second definition
 for tiny rows that pins the fp64 code.
 
-Inputs are numpy arrays: ``float32`` for fp32 data, or ``uint16`` holding
-bfloat16 bit patterns for bf16 data.  Outputs are ``float64``.
+Inputs are numpy arrays: ``float32`` for fp32 data, ``uint16`` holding
+bfloat16 bit patterns for bf16 data, ``float16`` for fp16 data (decoded by the
+oracle's own binary16 code).  Outputs are ``float64``.
 """
 from __future__ import annotations
 
@@ -27,6 +28,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32 = 0
 BF16 = 1
+F16 = 2
 
 
 def build(src: str = _SRC, out: str = _LIB) -> str:
@@ -79,7 +81,9 @@ class Oracle:
             return F32
         if a.dtype == np.uint16:
             return BF16
-        raise TypeError(f"oracle takes float32 or uint16 (bf16 bits), got {a.dtype}")
+        if a.dtype == np.float16:
+            return F16
+        raise TypeError(f"oracle takes float32, uint16 (bf16 bits) or float16, got {a.dtype}")
 
     @staticmethod
     def _ptr(a):

@@ -44,7 +44,7 @@
  *    of the last axis).
  *
  * Element types: 0 = IEEE binary32, 1 = bfloat16 (the upper 16 bits of a
- * binary32).  Both widen to double without rounding.
+ * binary32), 2 = IEEE binary16.  All widen to double without rounding.
  *
  * parity pins: every function here is pinned by the CPU tests (closed-form
  * hand cases, exact rational brute force, invariants, special cases).
@@ -55,6 +55,25 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_F16 2
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits; exponent 0 holds zeros and subnormals (fraction * 2^-24), exponent
+ * 31 holds infinities (fraction 0) and NaNs. */
+static double half_to_double(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int exponent = (h >> 10) & 0x1f;
+    const int fraction = h & 0x3ff;
+    double v;
+    if (exponent == 0)
+        v = ldexp((double)fraction, -24);
+    else if (exponent == 31)
+        v = fraction ? NAN : INFINITY;
+    else
+        v = ldexp((double)(fraction | 0x400), exponent - 25);
+    return sign ? -v : v;
+}
 
 /* Widen element i of a buffer of the given element type to double. */
 static double widen(const void *p, int dtype, int64_t i)
@@ -63,6 +82,8 @@ static double widen(const void *p, int dtype, int64_t i)
         const float *f = (const float *)p;
         return (double)f[i];
     }
+    if (dtype == ORACLE_F16)
+        return half_to_double(((const uint16_t *)p)[i]);
     /* bfloat16: the stored 16 bits are the high half of a binary32. */
     const uint16_t *h = (const uint16_t *)p;
     uint32_t bits = ((uint32_t)h[i]) << 16;

@@ -20,8 +20,9 @@ What pins what:
   invariances            LayerNorm(x + c) = LayerNorm(x); RMS(a x) = RMS(x)
   affine structure       y(w, b) = y(1, 0) * w + b, column-indexed weights
   row independence       permuting rows permutes outputs, bitwise
-  bf16 decoding          hand-built bf16 bit patterns decode to the values
-                         the format defines
+  bf16 / f16 decoding    hand-built bf16 and binary16 bit patterns (normal,
+                         subnormal, largest, inf, NaN) decode to the values
+                         the formats define
   dual q/k               each half against exact brute force, queries first
   RoPE                   golden values of the `rope` / `rope_with_freqs` doc
                          inputs from a complex-number formulation
@@ -99,13 +100,16 @@ def _tiny_rows(rng, dtype, width, rows):
     if dtype == "bf16":
         xb, wb, bb = _bf16_from_f32(x), _bf16_from_f32(w), _bf16_from_f32(b)
         return (xb, wb, bb), (_bf16_values(xb), _bf16_values(wb), _bf16_values(bb))
+    if dtype == "f16":
+        xh, wh, bh = x.astype(np.float16), w.astype(np.float16), b.astype(np.float16)
+        return (xh, wh, bh), (xh.astype(np.float64), wh.astype(np.float64), bh.astype(np.float64))
     return (x, w, b), (x.astype(np.float64), w.astype(np.float64), b.astype(np.float64))
 
 
 def pin_exact_bruteforce_rms(o):
     rng = np.random.default_rng(101)
     for width in range(1, 17):
-        for dtype in ("f32", "bf16"):
+        for dtype in ("f32", "bf16", "f16"):
             (x, w, _), (xv, wv, _) = _tiny_rows(rng, dtype, width, 3)
             eps = f32(rng.choice([0.0, 1e-6, 1e-5, 0.5]))
             got = o.rms(x, w, eps)
@@ -116,7 +120,7 @@ def pin_exact_bruteforce_rms(o):
 def pin_exact_bruteforce_layer(o):
     rng = np.random.default_rng(202)
     for width in range(1, 17):
-        for dtype in ("f32", "bf16"):
+        for dtype in ("f32", "bf16", "f16"):
             for use_bias in (True, False):
                 (x, w, b), (xv, wv, bv) = _tiny_rows(rng, dtype, width, 3)
                 eps = f32(rng.choice([1e-6, 1e-5, 0.5]))
@@ -237,6 +241,28 @@ def pin_bf16_decoding(o):
            what="bf16 decode (layer)")
 
 
+def pin_f16_decoding(o):
+    # binary16: sign | 5 exponent bits (bias 15) | 10 fraction bits
+    # 0x3C00 = 1, 0xC000 = -2, 0x3555 = 0.333251953125, 0x7BFF = 65504 (largest),
+    # 0x0400 = 2^-14 (smallest normal), 0x0001 = 2^-24 (smallest subnormal),
+    # 0x8200 = -2^-15 (subnormal)
+    bits = np.array([0x3C00, 0xC000, 0x3555, 0x7BFF, 0x0400, 0x0001, 0x8200], np.uint16)
+    vals = [1.0, -2.0, 0.333251953125, 65504.0, 2.0 ** -14, 2.0 ** -24, -2.0 ** -15]
+    ones = np.ones(1, np.float16)
+    x = bits.view(np.float16).reshape(7, 1)
+    got = o.rms(x, ones, 0.0)                    # width 1, eps 0: x / |x| = sign(x)
+    assert np.array_equal(got[:, 0], np.sign(vals)), "f16 decode (sign)"
+    # eps = 1: y = x / sqrt(x^2 + 1), invertible: x = y / sqrt(1 - y^2)
+    got = o.rms(x, ones, 1.0)[:, 0]
+    sel = [0, 1, 2, 4, 5, 6]
+    back = got[sel] / np.sqrt(1.0 - got[sel] ** 2)
+    _close(back, np.array(vals)[sel], 1e-12, what="f16 decode (values)")
+    assert abs(got[3] - 65504.0 / np.sqrt(65504.0 ** 2 + 1)) < 1e-15
+    inf = np.array([[0x7C00], [0xFC00], [0x7E00]], np.uint16).view(np.float16)
+    r = o.rms(inf, ones, 1.0)[:, 0]
+    assert np.isnan(r).all(), "f16 inf/nan decode (inf/inf and nan)"
+
+
 def pin_dual(o):
     rng = np.random.default_rng(909)
     for dtype in ("f32", "bf16"):
@@ -344,5 +370,5 @@ def pin_dual_rope(o):
 PINS = [pin_golden_hand_cases, pin_exact_bruteforce_rms, pin_exact_bruteforce_layer,
         pin_rms_unit_invariant, pin_layer_moments, pin_library_identities,
         pin_special_cases, pin_invariances, pin_affine_structure, pin_row_independence,
-        pin_bf16_decoding, pin_dual, pin_rope_norm_and_identity, pin_rope_relative_position,
+        pin_bf16_decoding, pin_f16_decoding, pin_dual, pin_rope_norm_and_identity, pin_rope_relative_position,
         pin_rope_composition_and_scale, pin_rope_layouts_and_table, pin_dual_rope]

@@ -51,6 +51,13 @@ MUTANTS = {
                              "oracle_rms(k, qw, dtype, k_rows, head_dim, eps, ky);"),
     "dual_eps_dropped_for_keys": ("oracle_rms(k, kw, dtype, k_rows, head_dim, eps, ky);",
                                   "oracle_rms(k, kw, dtype, k_rows, head_dim, 0.0f, ky);"),
+    "f16_exponent_bias": ("v = ldexp((double)(fraction | 0x400), exponent - 25);",
+                          "v = ldexp((double)(fraction | 0x400), exponent - 24);"),
+    "f16_no_implicit_bit": ("v = ldexp((double)(fraction | 0x400), exponent - 25);",
+                            "v = ldexp((double)(fraction), exponent - 25);"),
+    "f16_subnormal_scale": ("v = ldexp((double)fraction, -24);",
+                            "v = ldexp((double)fraction, -25);"),
+    "f16_sign_dropped": ("return sign ? -v : v;", "return v;"),
     "rope_sign": ("x[a] = xa * c - xb * s;", "x[a] = xa * c + xb * s;"),
     "rope_cos_sin_swapped": ("double c = cos(theta), s = sin(theta);",
                              "double c = sin(theta), s = cos(theta);"),
