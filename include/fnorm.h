@@ -13,9 +13,10 @@
  *  - x, w, b and y are DEVICE pointers owned by the caller; they must stay
  *    valid until the work queued on `stream` has completed.  The library
  *    allocates nothing, frees nothing and never synchronizes.
- *  - All tensors of one call share one element type `dtype` (fnorm_dtype);
- *    the output has the input's type.  Arithmetic is fp32; a bf16 output is
- *    the fp32 result rounded once, to nearest even.
+ *  - All tensors of one call share one element type `dtype` (fnorm_dtype:
+ *    fp32, bf16 or IEEE fp16); the output has the input's type.  Arithmetic
+ *    is fp32; a bf16 or fp16 output is the fp32 result rounded once, to
+ *    nearest even.
  *  - eps is fixed per call, must be finite and >= 0, and is added inside the
  *    square root.
  *  - `stream` is a hipStream_t; NULL means the null stream.  Calls return as
@@ -41,7 +42,7 @@
 extern "C" {
 #endif
 
-typedef enum { FNORM_F32 = 0, FNORM_BF16 = 1 } fnorm_dtype;
+typedef enum { FNORM_F32 = 0, FNORM_BF16 = 1, FNORM_F16 = 2 } fnorm_dtype;
 
 typedef enum {
     FNORM_OK = 0,

@@ -2,7 +2,8 @@
 reference values, ulp distance and the tolerance checks.
 
 Tolerances (fp32: relative error <= 1e-5; bf16: <= 1 ulp and <= 7.9e-3
-relative):
+relative; fp16: <= 1 ulp and <= 2^-10 relative, the relative error floored
+at fp16's smallest normal 2^-14 where its spacing becomes absolute):
   RMSNorm      |y - r| / |r|                 (0/0 counts as 0)
   LayerNorm    |y - r| / max(|r|, |w_j|)     (a floor at the scale of one
                                               normalized entry, since
@@ -20,12 +21,15 @@ import torch
 F32_REL_TOL = 1e-5
 BF16_REL_TOL = 2.0 ** -7      # 7.8125e-3 <= 7.9e-3
 BF16_MAX_ULP = 1
+F16_REL_TOL = 2.0 ** -10      # one fp16 ulp, relative, at worst
+F16_MAX_ULP = 1
+F16_MIN_NORMAL = 2.0 ** -14
 
 
 def to_oracle_array(t: torch.Tensor) -> np.ndarray:
-    """Host numpy view the oracle takes: float32, or uint16 bf16 bits."""
+    """Host numpy view the oracle takes: float32, uint16 bf16 bits, or float16."""
     t = t.detach().cpu().contiguous()
-    if t.dtype == torch.float32:
+    if t.dtype in (torch.float32, torch.float16):
         return t.numpy()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
@@ -69,6 +73,17 @@ def ulp_distance_bf16(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
     return np.abs(_ordered(a_bits) - _ordered(b_bits))
 
 
+def f16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def rne_f16_bits(r: np.ndarray) -> np.ndarray:
+    """float64 values rounded to IEEE binary16 (numpy rounds directly from
+    double, to nearest even); uint16 bit patterns."""
+    with np.errstate(over="ignore"):
+        return np.asarray(r, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
 def rel_err(y: np.ndarray, r: np.ndarray, floor: np.ndarray | None = None) -> np.ndarray:
     """|y - r| / max(|r|, floor), with 0/0 := 0 and matching NaNs := 0."""
     denom = np.abs(r) if floor is None else np.maximum(np.abs(r), np.abs(floor))
@@ -98,6 +113,20 @@ def check(op: str, y: torch.Tensor, r: np.ndarray, w: torch.Tensor | None = None
     assert nan_mismatch == 0, f"{label}: NaN positions differ ({nan_mismatch})"
     if y.dtype == torch.float32:
         assert out["max_rel"] <= F32_REL_TOL, f"{label}: fp32 rel err {out['max_rel']:.3e}"
+    elif y.dtype == torch.float16:
+        # below the smallest normal (2^-14) fp16 has a fixed absolute spacing,
+        # so relative error is measured against that floor; the ulp check
+        # below covers the subnormal range exactly
+        f16_floor = np.full(r.shape, F16_MIN_NORMAL) if floor is None else np.maximum(
+            np.abs(floor), F16_MIN_NORMAL)
+        out["max_rel"] = float(np.max(rel_err(yd, r, f16_floor))) if r.size else 0.0
+        assert out["max_rel"] <= F16_REL_TOL, f"{label}: fp16 rel err {out['max_rel']:.3e}"
+        ulps = ulp_distance_bf16(f16_bits(y).reshape(r.shape), rne_f16_bits(r))
+        if floor is not None:
+            ulps = np.where(np.abs(r) >= np.abs(floor), ulps, 0)
+        ulps = np.where(np.isfinite(r), ulps, 0)
+        out["max_ulp"] = int(ulps.max()) if ulps.size else 0
+        assert out["max_ulp"] <= F16_MAX_ULP, f"{label}: fp16 ulp distance {out['max_ulp']}"
     else:
         assert out["max_rel"] <= BF16_REL_TOL, f"{label}: bf16 rel err {out['max_rel']:.3e}"
         ulps = ulp_distance_bf16(bf16_bits(y).reshape(r.shape), rne_bf16_bits(r))

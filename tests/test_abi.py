@@ -72,7 +72,7 @@ def test_layer_validation(lib):
     assert lib.fnorm_layer(A, B, C - 8, C, 4, 8, 1e-5, F32, None) == 5    # y overlaps b
     assert lib.fnorm_layer(A, None, C, B, 4, 8, 1e-5, F32, None) == 1
     assert lib.fnorm_layer(A, B, None, C, 4, 8, -1.0, F32, None) == 3
-    assert lib.fnorm_layer(A, B, None, C, 4, 8, 1e-5, 2, None) == 4
+    assert lib.fnorm_layer(A, B, None, C, 4, 8, 1e-5, 3, None) == 4
     assert lib.fnorm_last_error().startswith(b"fnorm_layer: ")
 
 

@@ -26,6 +26,10 @@ def say(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def dcode(dtype):
+    return {torch.float32: trn.F32, torch.bfloat16: trn.BF16, torch.float16: trn.F16}[dtype]
+
+
 @pytest.fixture(scope="module")
 def o():
     return oracle.default()
@@ -130,7 +134,8 @@ SWEEP_WIDTHS = [1, 2, 3, 5, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 
                 2048, 2056, 3000, 4095, 4096, 4104, 5120, 8191, 8192, 8200, 12288, 16384]
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16],
+                         ids=["f32", "bf16", "f16"])
 @pytest.mark.parametrize("op", ["rms", "layer", "layer_nobias"])
 def test_width_sweep(o, op, dtype):
     for i, width in enumerate(SWEEP_WIDTHS):
@@ -140,7 +145,7 @@ def test_width_sweep(o, op, dtype):
                                with_bias=(op == "layer"))
         eps = 1e-5
         say(f"[sweep] {op} {dtype} rows={rows} width={width} "
-            f"kernel={trn.describe(trn.OP_RMS if base == 'rms' else trn.OP_LAYER, trn.F32 if dtype == torch.float32 else trn.BF16, width)}")
+            f"kernel={trn.describe(trn.OP_RMS if base == 'rms' else trn.OP_LAYER, dcode(dtype), width)}")
         y = run_gpu(base, t, eps)
         helpers.check(base, y, run_oracle(o, base, t, eps), t["w"], f"{op} w={width}")
 
@@ -152,7 +157,9 @@ VARIANT_CASES = [("rms", torch.bfloat16, 128), ("rms", torch.bfloat16, 768),
                  ("layer", torch.bfloat16, 4096), ("layer", torch.bfloat16, 8192),
                  ("layer", torch.float32, 768), ("layer", torch.float32, 1024),
                  ("layer", torch.bfloat16, 2048), ("rms", torch.float32, 8192),
-                 ("layer", torch.bfloat16, 100), ("rms", torch.float32, 3)]
+                 ("layer", torch.bfloat16, 100), ("rms", torch.float32, 3),
+                 ("rms", torch.float16, 4096), ("layer", torch.float16, 4096),
+                 ("rms", torch.float16, 8192), ("layer", torch.float16, 768)]
 
 
 @pytest.mark.parametrize("op,dtype,width", VARIANT_CASES,
@@ -163,7 +170,7 @@ def test_every_variant(o, op, dtype, width):
     t = inputs.random_rows(op, rows, width, dtype, seed=width, mean=1.0, std=2.0)
     eps = 1e-5
     r = run_oracle(o, op, t, eps)
-    code = trn.F32 if dtype == torch.float32 else trn.BF16
+    code = dcode(dtype)
     opc = trn.OP_RMS if op == "rms" else trn.OP_LAYER
     n = trn.variant_count(opc, code, width)
     assert n >= 4
@@ -175,13 +182,13 @@ def test_every_variant(o, op, dtype, width):
 
 @pytest.mark.parametrize("hd", [64, 80, 96, 128, 256, 100, 512, 1024])
 def test_dual_equals_two_singles(o, hd):
-    for dtype in (torch.bfloat16, torch.float32):
+    for dtype in (torch.bfloat16, torch.float32, torch.float16):
         g = torch.Generator().manual_seed(hd)
         q = torch.randn(33, 5, hd, generator=g).to(dtype).to(DEV)
         k = torch.randn(33, 2, hd, generator=g).to(dtype).to(DEV)
         qw = (1 + 0.1 * torch.randn(hd, generator=g)).to(dtype).to(DEV)
         kw = (1 + 0.1 * torch.randn(hd, generator=g)).to(dtype).to(DEV)
-        code = trn.F32 if dtype == torch.float32 else trn.BF16
+        code = dcode(dtype)
         n = trn.variant_count(trn.OP_DUAL, code, hd)
         say(f"[dual] hd={hd} {dtype} variants={n}")
         sq = trn.rms_norm(q, qw, 1e-6)
@@ -226,7 +233,7 @@ def test_rows_zero_one_two(o):
 def test_misaligned_pointers(o):
     """Tensors that start one element past a 16-byte boundary use the
     scalar-access kernels and give the same results."""
-    for dtype in (torch.float32, torch.bfloat16):
+    for dtype in (torch.float32, torch.bfloat16, torch.float16):
         for op in ("rms", "layer"):
             t = inputs.random_rows(op, 50, 1024, dtype, seed=77)
             big = torch.empty(50 * 1024 + 1, dtype=dtype, device=DEV)
@@ -290,7 +297,7 @@ def test_deterministic():
 
 def test_special_rows(o):
     """Zero rows, constant rows, NaN and infinity propagate as the oracle says."""
-    for dtype in (torch.float32, torch.bfloat16):
+    for dtype in (torch.float32, torch.bfloat16, torch.float16):
         x = torch.randn(8, 256).to(dtype)
         x[1] = 0.0                    # zero row: RMS gives zeros
         x[2] = 3.0                    # constant row: LayerNorm gives the bias
@@ -363,6 +370,7 @@ def test_describe_matches_hot_configs():
 
 # ----------------------------------------------------------------- composed baselines
 COMPOSED_CASES = [("rms", torch.float32, 512, 1024), ("layer", torch.float32, 1024, 768),
+                  ("rms", torch.float16, 256, 4096), ("layer", torch.float16, 100, 1000),
                   ("rms", torch.bfloat16, 1024, 8192), ("layer", torch.bfloat16, 2048, 4096),
                   ("rms", torch.bfloat16, 37, 100), ("layer", torch.float32, 37, 1001),
                   ("layer", torch.bfloat16, 64, 128), ("rms", torch.float32, 3, 7)]
@@ -426,6 +434,8 @@ ROPE_CASES = [  # (dtype, tokens, q_heads, k_heads, head_dim, dims, traditional,
     (torch.float32, 17, 2, 1, 1024, 1024, False, 10000.0, 1.0, 12345, False),
     (torch.bfloat16, 1, 1, 0, 128, 128, False, 10000.0, 1.0, 9, False),
     (torch.bfloat16, 5, 0, 4, 128, 128, True, 10000.0, 1.0, 9, False),
+    (torch.float16, 130, 32, 8, 128, 128, False, 10000.0, 1.0, 2048, False),
+    (torch.float16, 40, 4, 4, 64, 64, True, 10000.0, 1.0, 3, False),
 ]
 
 
@@ -441,7 +451,7 @@ def test_dual_rope_matches_oracle(o, case):
     if table:
         freqs = (base ** (-torch.arange(0, dims, 2, dtype=torch.float64) / dims)
                  * (1 + 0.3 * torch.rand(dims // 2, generator=g, dtype=torch.float64))).float()
-    code = trn.F32 if dtype == torch.float32 else trn.BF16
+    code = dcode(dtype)
     n = trn.rope_variant_count(code, hd, dims, trad)
     assert n >= 2
     rq, rk = o.dual_head_rms_rope(helpers.to_oracle_array(q), helpers.to_oracle_array(k),

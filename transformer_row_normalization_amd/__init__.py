@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfnorm.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "fnorm.h")
 
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 OP_RMS, OP_LAYER, OP_DUAL = 0, 1, 2
 STATUS = {0: "FNORM_OK", 1: "FNORM_ERR_NULL", 2: "FNORM_ERR_SHAPE", 3: "FNORM_ERR_EPS",
           4: "FNORM_ERR_DTYPE", 5: "FNORM_ERR_ALIAS", 6: "FNORM_ERR_UNSUPPORTED",
@@ -106,7 +106,9 @@ def _dtype_code(t) -> int:
         return F32
     if t.dtype == torch.bfloat16:
         return BF16
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype == torch.float16:
+        return F16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float16)")
 
 
 def _stream(t) -> int:

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfnorm.so")
-SOURCES = ["fnorm_api.hip", "fnorm_inst_f32.hip", "fnorm_inst_bf16.hip", "fnorm_composed.hip", "fnorm_inst_rope.hip"]
+SOURCES = ["fnorm_api.hip", "fnorm_inst_f32.hip", "fnorm_inst_bf16.hip", "fnorm_inst_f16.hip", "fnorm_composed.hip", "fnorm_inst_rope.hip"]
 ARCH = "gfx950"
 HIP_FLAGS = ["-O3", f"--offload-arch={ARCH}", "-std=c++17", "-fPIC", "-ffp-contract=off",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -52,6 +52,7 @@ const Registry& registry() {
         Registry reg;
         register_f32(reg.table);
         register_bf16(reg.table);
+        register_f16(reg.table);
         register_rope(reg.table);
         reg.occupancy.reset(new std::atomic<int>[reg.table.size()]);
         for (size_t i = 0; i < reg.table.size(); ++i) reg.occupancy[i].store(0);
@@ -60,8 +61,13 @@ const Registry& registry() {
     return r;
 }
 
+bool valid_dtype(int dtype) {
+    return dtype == FNORM_F32 || dtype == FNORM_BF16 || dtype == FNORM_F16;
+}
 int elem_bytes(int dtype) { return dtype == FNORM_F32 ? 4 : 2; }
-const char* dtype_name(int dtype) { return dtype == FNORM_F32 ? "f32" : "bf16"; }
+const char* dtype_name(int dtype) {
+    return dtype == FNORM_F32 ? "f32" : dtype == FNORM_BF16 ? "bf16" : "f16";
+}
 
 // One runnable choice: a table entry plus the grid policy.
 struct Choice {
@@ -203,8 +209,9 @@ bool overlap(const void* a, int64_t an, const void* b, int64_t bn) {
 }
 
 int check_scalars(const char* op, int dtype, int64_t rows, int64_t width, float eps) {
-    if (dtype != FNORM_F32 && dtype != FNORM_BF16)
-        return fail(FNORM_ERR_DTYPE, op, "dtype %d is not FNORM_F32 (0) or FNORM_BF16 (1)", dtype);
+    if (!valid_dtype(dtype))
+        return fail(FNORM_ERR_DTYPE, op, "dtype %d is not FNORM_F32 (0), FNORM_BF16 (1) or FNORM_F16 (2)",
+                    dtype);
     if (rows < 0 || width <= 0)
         return fail(FNORM_ERR_SHAPE, op, "rows=%lld width=%lld (need rows >= 0, width > 0)",
                     (long long)rows, (long long)width);
@@ -456,7 +463,7 @@ int fnorm_dual_head_rms_rope(const void* q, const void* k, const void* qw, const
 }
 
 int fnorm_variant_count(int op, int dtype, int64_t width, int aligned) {
-    if ((dtype != FNORM_F32 && dtype != FNORM_BF16) || width <= 0 || op < 0 || op > 2) return 0;
+    if (!valid_dtype(dtype) || width <= 0 || op < 0 || op > 2) return 0;
     const Variant* list[kMaxCandidates];
     return 2 * candidates(op_kind(op, true), dtype, width, aligned != 0, list);
 }
@@ -466,8 +473,7 @@ int fnorm_describe(int op, int dtype, int64_t width, int aligned, int variant, c
     static const char* name = "fnorm_describe";
     if (!buf || len <= 0) return fail(FNORM_ERR_NULL, name, "buf must be non-NULL, len > 0");
     buf[0] = '\0';
-    if (dtype != FNORM_F32 && dtype != FNORM_BF16)
-        return fail(FNORM_ERR_DTYPE, name, "dtype %d", dtype);
+    if (!valid_dtype(dtype)) return fail(FNORM_ERR_DTYPE, name, "dtype %d", dtype);
     if (width <= 0) return fail(FNORM_ERR_SHAPE, name, "width %lld", (long long)width);
     if (op < 0 || op > 2) return fail(FNORM_ERR_UNSUPPORTED, name, "op %d", op);
     Choice c;
@@ -479,7 +485,7 @@ int fnorm_describe(int op, int dtype, int64_t width, int aligned, int variant, c
 
 int fnorm_rope_variant_count(int dtype, int64_t head_dim, int64_t rope_dims, int traditional,
                              int aligned) {
-    if ((dtype != FNORM_F32 && dtype != FNORM_BF16) || head_dim <= 0 || rope_dims < 2 ||
+    if (!valid_dtype(dtype) || head_dim <= 0 || rope_dims < 2 ||
         rope_dims % 2 != 0 || rope_dims > head_dim)
         return 0;
     const Variant* list[kMaxCandidates];

@@ -200,6 +200,12 @@ hipError_t run(bool layer, const void* x, const void* w, const void* b, void* y,
                                : layer_chain<DT_F32, 1>(L, x, w, b, y, eps, ws);
         return vec4 ? rms_chain<DT_F32, 4>(L, x, w, y, eps, ws) : rms_chain<DT_F32, 1>(L, x, w, y, eps, ws);
     }
+    if (dtype == DT_F16) {
+        if (layer) return vec4 ? layer_chain<DT_F16, 4>(L, x, w, b, y, eps, ws)
+                               : layer_chain<DT_F16, 1>(L, x, w, b, y, eps, ws);
+        return vec4 ? rms_chain<DT_F16, 4>(L, x, w, y, eps, ws)
+                    : rms_chain<DT_F16, 1>(L, x, w, y, eps, ws);
+    }
     if (layer) return vec4 ? layer_chain<DT_BF16, 4>(L, x, w, b, y, eps, ws)
                            : layer_chain<DT_BF16, 1>(L, x, w, b, y, eps, ws);
     return vec4 ? rms_chain<DT_BF16, 4>(L, x, w, y, eps, ws) : rms_chain<DT_BF16, 1>(L, x, w, y, eps, ws);

@@ -3,9 +3,9 @@
 //  * Raw element packs: 16-byte vectors (4 x fp32 or 8 x bf16) for the
 //    coalesced path, single elements for the scalar path.  Rows stay in
 //    registers as raw bits and are widened to fp32 at each use.
-//  * bf16 <-> fp32: widening is a shift (bf16 is the high half of a
-//    binary32); narrowing is round-to-nearest-even via gfx950's packed
-//    v_cvt_pk_bf16_f32.
+//  * bf16 / fp16 <-> fp32: bf16 widens by a shift (it is the high half of a
+//    binary32), fp16 by v_cvt_f32_f16; narrowing is round-to-nearest-even
+//    through gfx950's packed converts.
 //  * Cross-lane sums with a fixed butterfly: after each step every lane of
 //    the group holds the same bits (a + b computed in both lanes of a pair
 //    is the same IEEE result), so row scalars are identical in every lane
@@ -17,13 +17,14 @@
 
 namespace fnorm {
 
-enum : int { DT_F32 = 0, DT_BF16 = 1 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 enum : int { OP_RMS = 0, OP_LAYER = 1 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- packs
 template <int DT, int VEC> struct Raw;
@@ -32,10 +33,14 @@ template <> struct Raw<DT_BF16, 8> { using type = u32x4; };
 template <> struct Raw<DT_BF16, 4> { using type = u32x2; };
 template <> struct Raw<DT_F32, 1> { using type = uint32_t; };
 template <> struct Raw<DT_BF16, 1> { using type = uint16_t; };
+template <> struct Raw<DT_F16, 8> { using type = u32x4; };
+template <> struct Raw<DT_F16, 4> { using type = u32x2; };
+template <> struct Raw<DT_F16, 1> { using type = uint16_t; };
 
 template <int DT> struct Elem;
 template <> struct Elem<DT_F32> { static constexpr int bytes = 4; };
 template <> struct Elem<DT_BF16> { static constexpr int bytes = 2; };
+template <> struct Elem<DT_F16> { static constexpr int bytes = 2; };
 
 template <int DT, int VEC>
 __device__ __forceinline__ typename Raw<DT, VEC>::type raw_zero() {
@@ -67,13 +72,23 @@ __device__ __forceinline__ void store_raw(void* base, int64_t idx, typename Raw<
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
+__device__ __forceinline__ float f16_val(uint32_t h16) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h16)));
+}
+
+// A 16-bit element (bf16 or fp16) widened to fp32, exactly.
+template <int DT>
+__device__ __forceinline__ float widen16(uint32_t bits16) {
+    if constexpr (DT == DT_BF16) return __builtin_bit_cast(float, bits16 << 16);
+    else return f16_val(bits16 & 0xFFFFu);
+}
 
 // Element i of a pack, widened to fp32 (exact).
 template <int DT, int VEC>
 __device__ __forceinline__ float elem(const typename Raw<DT, VEC>::type& r, int i) {
     if constexpr (VEC == 1) {
         if constexpr (DT == DT_F32) return __builtin_bit_cast(float, r);
-        else return __builtin_bit_cast(float, uint32_t(r) << 16);
+        else return widen16<DT>(uint32_t(r));
     } else if constexpr (DT == DT_F32) {
         // Copy the component out first: bit_cast of a vector-component
         // lvalue reads component 0 whatever the index.
@@ -81,14 +96,23 @@ __device__ __forceinline__ float elem(const typename Raw<DT, VEC>::type& r, int 
         return __builtin_bit_cast(float, u);
     } else {
         const uint32_t u = r[i >> 1];
-        return (i & 1) ? bf16_hi(u) : bf16_lo(u);
+        if constexpr (DT == DT_BF16) return (i & 1) ? bf16_hi(u) : bf16_lo(u);
+        else return f16_val((i & 1) ? (u >> 16) : (u & 0xFFFFu));
     }
 }
 
-// Two fp32 values rounded to bf16 (nearest, ties to even), packed lo | hi << 16.
+// Two fp32 values rounded (nearest, ties to even) to the 16-bit type,
+// packed lo | hi << 16 (gfx950 packed converts).
+template <int DT>
+__device__ __forceinline__ uint32_t pack16x2(float lo, float hi) {
+    if constexpr (DT == DT_BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    bf16x2 h = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
-    return __builtin_bit_cast(uint32_t, h);
+    return pack16x2<DT_BF16>(lo, hi);
 }
 
 // VEC fp32 values stored into a pack of the element type.
@@ -96,15 +120,15 @@ template <int DT, int VEC>
 __device__ __forceinline__ typename Raw<DT, VEC>::type make_raw(const float (&f)[VEC]) {
     if constexpr (VEC == 1) {
         if constexpr (DT == DT_F32) return __builtin_bit_cast(uint32_t, f[0]);
-        else return uint16_t(pack_bf16x2(f[0], 0.0f) & 0xFFFFu);
+        else return uint16_t(pack16x2<DT>(f[0], 0.0f) & 0xFFFFu);
     } else if constexpr (DT == DT_F32) {
         return u32x4{__builtin_bit_cast(uint32_t, f[0]), __builtin_bit_cast(uint32_t, f[1]),
                      __builtin_bit_cast(uint32_t, f[2]), __builtin_bit_cast(uint32_t, f[3])};
     } else if constexpr (VEC == 4) {
-        return u32x2{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+        return u32x2{pack16x2<DT>(f[0], f[1]), pack16x2<DT>(f[2], f[3])};
     } else {
-        return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                     pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+        return u32x4{pack16x2<DT>(f[0], f[1]), pack16x2<DT>(f[2], f[3]),
+                     pack16x2<DT>(f[4], f[5]), pack16x2<DT>(f[6], f[7])};
     }
 }
 

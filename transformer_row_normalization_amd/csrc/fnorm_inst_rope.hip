@@ -64,6 +64,7 @@ void register_rope_dtype(std::vector<Variant>& t) {
 void register_rope(std::vector<Variant>& table) {
     register_rope_dtype<DT_F32>(table);
     register_rope_dtype<DT_BF16>(table);
+    register_rope_dtype<DT_F16>(table);
 }
 
 }  // namespace fnorm

@@ -38,6 +38,7 @@ struct Variant {
 // instance of that element type, in preference order.
 void register_f32(std::vector<Variant>& table);
 void register_bf16(std::vector<Variant>& table);
+void register_f16(std::vector<Variant>& table);
 // Defined in fnorm_inst_rope.hip: the fused dual norm + RoPE instances.
 void register_rope(std::vector<Variant>& table);
 
