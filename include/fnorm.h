@@ -5,7 +5,8 @@
  *
  * Common conventions
  * ------------------
- *  - Tensors are contiguous, row-major [rows, width]; the normalization runs
+ *  - Tensors are row-major [rows, width], contiguous unless a call takes
+ *    strides (the _strided forms below); the normalization runs
  *    over the last axis only (the fused kernels' contract in the
  *    Emily.Bumblebee.FastKernels docs, "What's not rewritten": norms over any
  *    other axis are not served).  rows is the product of the leading
@@ -136,6 +137,49 @@ int fnorm_layer_v(const void* x, const void* w, const void* b, void* y, int64_t 
 int fnorm_dual_head_rms_v(const void* q, const void* k, const void* qw, const void* kw, void* qy,
                           void* ky, int64_t q_rows, int64_t k_rows, int64_t head_dim, float eps,
                           int dtype, void* stream, int variant);
+
+/*
+ * Row-strided forms, for rows that are not packed back to back: views into a
+ * wider buffer, such as the query and key parts of one packed QKV projection
+ * output (the ffai-argus `kernel_micro_ab.rs` example, section 2, where the
+ * packed QKV op writes the q and k buffers).  Strides count ELEMENTS of
+ * `dtype`, not bytes.
+ *   fnorm_rms_strided / fnorm_layer_strided: row r of x starts at
+ *     x + r * x_stride, row r of y at y + r * y_stride; the rows are `width`
+ *     contiguous elements.  Strides must be >= width when rows > 1.
+ *   fnorm_dual_head_rms_strided / fnorm_dual_head_rms_rope_strided: q is
+ *     [tokens, q_heads, head_dim] with the heads of one token contiguous and
+ *     token t at q + t * q_stride (likewise k, qy, ky with their strides);
+ *     every stride must be >= heads * head_dim of its tensor when
+ *     tokens > 1.  The dual form computes per-head RMSNorm exactly as
+ *     fnorm_dual_head_rms; the rope form exactly as fnorm_dual_head_rms_rope.
+ * An output may be its own input (same pointer and stride); otherwise an
+ * output must not share a byte with any other tensor of the call, which is
+ * checked exactly for tensors of equal stride (interleaved q/k/v parts of one
+ * buffer are accepted) and by overall extent otherwise.  The bytes between
+ * rows are neither read nor written.  16-byte vector kernels are used when
+ * the pointers are 16-byte aligned and every stride is a multiple of 16
+ * bytes; otherwise the scalar-access kernels.  variant as for the _v calls
+ * (-1 = default).  Other conventions as above.
+ */
+int fnorm_rms_strided(const void* x, int64_t x_stride, const void* w, void* y, int64_t y_stride,
+                      int64_t rows, int64_t width, float eps, int dtype, void* stream,
+                      int variant);
+int fnorm_layer_strided(const void* x, int64_t x_stride, const void* w, const void* b, void* y,
+                        int64_t y_stride, int64_t rows, int64_t width, float eps, int dtype,
+                        void* stream, int variant);
+int fnorm_dual_head_rms_strided(const void* q, int64_t q_stride, const void* k,
+                                int64_t k_stride, const void* qw, const void* kw, void* qy,
+                                int64_t qy_stride, void* ky, int64_t ky_stride, int64_t tokens,
+                                int64_t q_heads, int64_t k_heads, int64_t head_dim, float eps,
+                                int dtype, void* stream, int variant);
+int fnorm_dual_head_rms_rope_strided(const void* q, int64_t q_stride, const void* k,
+                                     int64_t k_stride, const void* qw, const void* kw, void* qy,
+                                     int64_t qy_stride, void* ky, int64_t ky_stride,
+                                     int64_t tokens, int64_t q_heads, int64_t k_heads,
+                                     int64_t head_dim, float eps, int64_t rope_dims,
+                                     int traditional, float base, float scale, int64_t offset,
+                                     const float* freqs, int dtype, void* stream, int variant);
 
 /*
  * Number of kernel variants able to serve (op, dtype, width) when every

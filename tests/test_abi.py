@@ -187,3 +187,62 @@ def test_rope_validation(lib):
     assert trn.rope_variant_count(BF16, 128, 128, True) >= 2
     assert "lpr16" in trn.describe_rope(BF16, 128, 128, False)
     assert trn.rope_variant_count(BF16, 128, 127, False) == 0
+
+
+def test_strided_row_validation(lib):
+    # (x, x_stride, w, y, y_stride, rows, width, eps, dtype, stream, variant)
+    rms = lambda *a: lib.fnorm_rms_strided(*a, F32, None, 10 ** 6)
+    assert rms(A, 7, B, C, 16, 4, 8, 1e-6) == 2           # x stride below width
+    assert rms(A, 16, B, C, 7, 4, 8, 1e-6) == 2           # y stride below width
+    assert rms(A, 1 << 60, B, C, 16, 4, 8, 1e-6) == 2     # stride overflow
+    assert rms(A, 16, B, A, 8, 4, 8, 1e-6) == 5           # y = x but another stride
+    assert rms(A, 16, B, A + 16, 16, 4, 8, 1e-6) == 5     # y rows shifted into x's rows
+    # y rows in the gaps between x's rows are accepted: variant 10**6 then
+    # fails as unsupported, which shows validation passed (nothing launches)
+    assert rms(A, 16, B, A + 32, 16, 4, 8, 1e-6) == 6     # x at A+64r, y at A+32+64r
+    assert rms(A, 32, B, A + 32, 32, 4, 8, 1e-6) == 6     # x at A+128r, y at A+32+128r
+    assert rms(A, 16, B, A, 16, 4, 8, 1e-6) == 6          # in place, same stride
+    assert rms(A, 16, B, C, 16, 1, 8, 1e-6) == 6          # one row: strides unused
+    assert rms(A, 3, B, C, 3, 1, 8, 1e-6) == 6
+    assert lib.fnorm_last_error().startswith(b"fnorm_rms_strided: ")
+    # (x, x_stride, w, b, y, y_stride, rows, width, eps)
+    lay = lambda *a: lib.fnorm_layer_strided(*a, F32, None, 10 ** 6)
+    assert lay(A, 8, B, None, C, 4, 4, 8, 1e-5) == 2      # y stride below width
+    assert lay(A, 16, B, A + 40, C, 16, 4, 8, 1e-5) == 6  # inputs may overlap each other
+    assert lay(A, 16, B, C + 8, C, 16, 4, 8, 1e-5) == 5   # y overlaps b
+    assert lib.fnorm_last_error().startswith(b"fnorm_layer_strided: ")
+
+
+def test_packed_qkv_layout_is_accepted(lib):
+    """q, k and v heads of one token packed back to back (one buffer, token
+    stride (qh + 2 kh) * hd): normalizing q and k in place is legal; an
+    output that lands on v, or on the other input, is not."""
+    hd, qh, kh, tokens = 128, 8, 2, 16
+    ts = (qh + 2 * kh) * hd                     # token stride, elements
+    eb = 2                                      # bf16
+    q = A
+    k = A + qh * hd * eb
+    v = A + (qh + kh) * hd * eb
+    D, E = 0x1000000, 0x2000000                 # weights elsewhere
+
+    def dual(qp, kp, qyp, kyp, qs=ts, ks=ts, qys=ts, kys=ts, variant=10 ** 6):
+        return lib.fnorm_dual_head_rms_strided(qp, qs, kp, ks, D, E, qyp, qys, kyp, kys, tokens,
+                                               qh, kh, hd, 1e-6, BF16, None, variant)
+    assert dual(q, k, q, k) == 6                # in place inside the packed buffer
+    assert dual(q, k, B, C, qys=qh * hd, kys=kh * hd) == 6   # to separate buffers
+    assert dual(q, k, q, v) == 6                # ky into v's slots: v is not an input
+    assert dual(q, k, v, k) == 5                # qy (8 heads) over v (2 heads) and beyond
+    assert dual(q, k, k, k) == 5                # qy over k
+    assert dual(q, k, q + 16, k) == 5           # qy shifted into q
+    assert dual(q, k, q, k, qs=qh * hd - 1) == 2  # q token stride below its heads
+    assert dual(q, k, q, k, ks=kh * hd - 1) == 2
+    assert lib.fnorm_last_error().startswith(b"fnorm_dual_head_rms_strided: ")
+
+    def rope(qp, kp, qyp, kyp, qs=ts, ks=ts, qys=ts, kys=ts):
+        return lib.fnorm_dual_head_rms_rope_strided(
+            qp, qs, kp, ks, D, E, qyp, qys, kyp, kys, tokens, qh, kh, hd, 1e-6, hd, 0, 10000.0,
+            1.0, 0, None, BF16, None, 10 ** 6)
+    assert rope(q, k, q, k) == 6
+    assert rope(q, k, k, k) == 5
+    assert rope(q, k, q, k, kys=kh * hd - 8) == 2
+    assert lib.fnorm_last_error().startswith(b"fnorm_dual_head_rms_rope_strided: ")

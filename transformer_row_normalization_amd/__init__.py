@@ -11,6 +11,8 @@ missing, every call raises.
   rms_norm(x, w, eps)                    RMSNorm over the last axis
   layer_norm(x, w, b, eps)               LayerNorm over the last axis (b optional)
   dual_head_rms_norm(q, k, qw, kw, eps)  q/k head RMSNorm in one launch
+  dual_head_rms_rope(q, k, qw, kw, eps)  the same, with RoPE fused in
+Row ops also take row-strided views (e.g. parts of a packed QKV buffer).
 """
 from __future__ import annotations
 
@@ -61,6 +63,13 @@ _SIGNATURES = {
                                     _F, _F, _I64, _P, _I, _P, _I], _I),
     "fnorm_rope_variant_count": ([_I, _I64, _I64, _I, _I], _I),
     "fnorm_describe_rope": ([_I, _I64, _I64, _I, _I, _I, ctypes.c_char_p, _I64], _I),
+    "fnorm_rms_strided": ([_P, _I64, _P, _P, _I64, _I64, _I64, _F, _I, _P, _I], _I),
+    "fnorm_layer_strided": ([_P, _I64, _P, _P, _P, _I64, _I64, _I64, _F, _I, _P, _I], _I),
+    "fnorm_dual_head_rms_strided": ([_P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _I64, _I64, _I64,
+                                     _I64, _I64, _F, _I, _P, _I], _I),
+    "fnorm_dual_head_rms_rope_strided": ([_P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _I64, _I64,
+                                          _I64, _I64, _I64, _F, _I64, _I, _F, _F, _I64, _P, _I,
+                                          _P, _I], _I),
     "fnorm_rms_composed": ([_P, _P, _P, _I64, _I64, _F, _I, _P, _I64, _P], _I),
     "fnorm_layer_composed": ([_P, _P, _P, _P, _I64, _I64, _F, _I, _P, _I64, _P], _I),
 }
@@ -129,35 +138,83 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def rms_norm(x, w, eps: float = 1e-6, out=None, variant: int = -1):
-    """y = x * rsqrt(mean(x^2, last axis) + eps) * w  (fp32 or bf16 CUDA tensors)."""
+def _check_dev(t, name, dtype, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _row_stride(t, name) -> int:
+    """Row stride (elements) of t seen as rows of its last axis: the last
+    axis must be unit-stride and the leading axes must nest into one evenly
+    strided row index (a slice of the last axis of a wider buffer does)."""
+    width = t.shape[-1] if t.dim() else 1
+    if t.dim() and width > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last axis must have stride 1")
+    lead = [(n, st) for n, st in zip(t.shape[:-1], t.stride()[:-1]) if n != 1]
+    if not lead:
+        return width
+    stride = expect = lead[-1][1]
+    for n, st in reversed(lead):
+        if st != expect:
+            raise ValueError(f"{name}: leading axes do not form evenly strided rows")
+        expect = st * n
+    return stride
+
+
+def _token_stride(t, name) -> int:
+    """Token stride of a [tokens, heads, head_dim] tensor whose heads of one
+    token are packed back to back."""
+    tokens, heads, hd = t.shape
+    if hd > 1 and t.stride(2) != 1:
+        raise ValueError(f"{name}: head_dim must have stride 1")
+    if heads > 1 and t.stride(1) != hd:
+        raise ValueError(f"{name}: the heads of one token must be contiguous")
+    return t.stride(0) if tokens > 1 else heads * hd
+
+
+def _rows_io(x, out, name="x"):
+    """Checks x and out for a row op; returns (y, rows, width, x_stride,
+    y_stride), strides None when both tensors are contiguous."""
     torch = _torch()
     if not x.is_cuda:
-        raise ValueError("x must be a GPU tensor")
-    code = _dtype_code(x)
-    _require(x, "x", x.dtype, x.device)
+        raise ValueError(f"{name} must be a GPU tensor")
+    _dtype_code(x)
+    _check_dev(x, name, x.dtype, x.device)
     width = x.shape[-1] if x.dim() else 1
-    _require(w, "w", x.dtype, x.device)
-    if tuple(w.shape) != (width,):
-        raise ValueError(f"w has shape {tuple(w.shape)}, expected ({width},)")
-    y = torch.empty_like(x) if out is None else out
-    _require(y, "out", x.dtype, x.device)
+    y = torch.empty(x.shape, dtype=x.dtype, device=x.device) if out is None else out
+    _check_dev(y, "out", x.dtype, x.device)
     if y.shape != x.shape:
         raise ValueError("out must have x's shape")
     rows = x.numel() // width if width else 0
-    _check(lib().fnorm_rms_v(_ptr(x), _ptr(w), _ptr(y), rows, width, eps, code, _stream(x),
-                             variant))
+    if x.is_contiguous() and y.is_contiguous():
+        return y, rows, width, None, None
+    return y, rows, width, _row_stride(x, name), _row_stride(y, "out")
+
+
+def rms_norm(x, w, eps: float = 1e-6, out=None, variant: int = -1):
+    """y = x * rsqrt(mean(x^2, last axis) + eps) * w  (fp32, bf16 or fp16 GPU
+    tensors).  x and out may be row-strided views (unit-stride last axis)."""
+    code = _dtype_code(x)
+    y, rows, width, xs, ys = _rows_io(x, out)
+    _require(w, "w", x.dtype, x.device)
+    if tuple(w.shape) != (width,):
+        raise ValueError(f"w has shape {tuple(w.shape)}, expected ({width},)")
+    if xs is None:
+        _check(lib().fnorm_rms_v(_ptr(x), _ptr(w), _ptr(y), rows, width, eps, code, _stream(x),
+                                 variant))
+    else:
+        _check(lib().fnorm_rms_strided(_ptr(x), xs, _ptr(w), _ptr(y), ys, rows, width, eps, code,
+                                       _stream(x), variant))
     return y
 
 
 def layer_norm(x, w, b=None, eps: float = 1e-5, out=None, variant: int = -1):
-    """y = (x - mean) * rsqrt(var + eps) * w + b over the last axis; b may be None."""
-    torch = _torch()
-    if not x.is_cuda:
-        raise ValueError("x must be a GPU tensor")
+    """y = (x - mean) * rsqrt(var + eps) * w + b over the last axis; b may be
+    None.  x and out may be row-strided views (unit-stride last axis)."""
     code = _dtype_code(x)
-    _require(x, "x", x.dtype, x.device)
-    width = x.shape[-1] if x.dim() else 1
+    y, rows, width, xs, ys = _rows_io(x, out)
     _require(w, "w", x.dtype, x.device)
     if tuple(w.shape) != (width,):
         raise ValueError(f"w has shape {tuple(w.shape)}, expected ({width},)")
@@ -165,38 +222,52 @@ def layer_norm(x, w, b=None, eps: float = 1e-5, out=None, variant: int = -1):
         _require(b, "b", x.dtype, x.device)
         if tuple(b.shape) != (width,):
             raise ValueError(f"b has shape {tuple(b.shape)}, expected ({width},)")
-    y = torch.empty_like(x) if out is None else out
-    _require(y, "out", x.dtype, x.device)
-    if y.shape != x.shape:
-        raise ValueError("out must have x's shape")
-    rows = x.numel() // width if width else 0
-    _check(lib().fnorm_layer_v(_ptr(x), _ptr(w), _ptr(b), _ptr(y), rows, width, eps, code,
-                               _stream(x), variant))
+    if xs is None:
+        _check(lib().fnorm_layer_v(_ptr(x), _ptr(w), _ptr(b), _ptr(y), rows, width, eps, code,
+                                   _stream(x), variant))
+    else:
+        _check(lib().fnorm_layer_strided(_ptr(x), xs, _ptr(w), _ptr(b), _ptr(y), ys, rows, width,
+                                         eps, code, _stream(x), variant))
     return y
 
 
 def dual_head_rms_norm(q, k, qw, kw, eps: float = 1e-6, q_out=None, k_out=None,
                        variant: int = -1):
     """One launch: (RMSNorm(q, qw), RMSNorm(k, kw)) over the head dimension
-    (last axis); queries first, keys second."""
+    (last axis); queries first, keys second.  Contiguous q and k of any
+    shape, or [tokens, heads, head_dim] views whose tokens are strided (the
+    q and k parts of a packed QKV buffer); outputs are written in place when
+    q_out is q and k_out is k."""
     torch = _torch()
     if not q.is_cuda:
         raise ValueError("q must be a GPU tensor")
     code = _dtype_code(q)
     hd = q.shape[-1]
     for t, n in ((q, "q"), (k, "k"), (qw, "qw"), (kw, "kw")):
-        _require(t, n, q.dtype, q.device)
+        _check_dev(t, n, q.dtype, q.device)
+    _require(qw, "qw", q.dtype, q.device)
+    _require(kw, "kw", q.dtype, q.device)
     if k.shape[-1] != hd or tuple(qw.shape) != (hd,) or tuple(kw.shape) != (hd,):
         raise ValueError("q, k, qw and kw must share the head dimension")
-    qy = torch.empty_like(q) if q_out is None else q_out
-    ky = torch.empty_like(k) if k_out is None else k_out
-    _require(qy, "q_out", q.dtype, q.device)
-    _require(ky, "k_out", q.dtype, q.device)
+    qy = torch.empty(q.shape, dtype=q.dtype, device=q.device) if q_out is None else q_out
+    ky = torch.empty(k.shape, dtype=k.dtype, device=k.device) if k_out is None else k_out
+    _check_dev(qy, "q_out", q.dtype, q.device)
+    _check_dev(ky, "k_out", q.dtype, q.device)
     if qy.shape != q.shape or ky.shape != k.shape:
         raise ValueError("outputs must match the inputs' shapes")
-    _check(lib().fnorm_dual_head_rms_v(_ptr(q), _ptr(k), _ptr(qw), _ptr(kw), _ptr(qy), _ptr(ky),
-                                       q.numel() // hd, k.numel() // hd, hd, eps, code,
-                                       _stream(q), variant))
+    if all(t.is_contiguous() for t in (q, k, qy, ky)):
+        _check(lib().fnorm_dual_head_rms_v(_ptr(q), _ptr(k), _ptr(qw), _ptr(kw), _ptr(qy),
+                                           _ptr(ky), q.numel() // hd, k.numel() // hd, hd, eps,
+                                           code, _stream(q), variant))
+        return qy, ky
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0]:
+        raise ValueError("strided q and k must be [tokens, heads, head_dim] views")
+    tokens, qh, _ = q.shape
+    kh = k.shape[1]
+    _check(lib().fnorm_dual_head_rms_strided(
+        _ptr(q), _token_stride(q, "q"), _ptr(k), _token_stride(k, "k"), _ptr(qw), _ptr(kw),
+        _ptr(qy), _token_stride(qy, "q_out"), _ptr(ky), _token_stride(ky, "k_out"), tokens, qh,
+        kh, hd, eps, code, _stream(q), variant))
     return qy, ky
 
 
@@ -252,7 +323,9 @@ def dual_head_rms_rope(q, k, qw, kw, eps: float = 1e-6, dims: int | None = None,
     q [tokens, q_heads, head_dim], k [tokens, k_heads, head_dim]; dims
     (default head_dim) features rotate, split-half pairs unless
     `traditional`; freqs: optional float32 GPU tensor of dims/2 inverse
-    frequencies replacing the base schedule; offset: position of token 0."""
+    frequencies replacing the base schedule; offset: position of token 0.
+    q, k and the outputs may be token-strided views (heads of one token
+    contiguous), e.g. the q and k parts of a packed QKV buffer."""
     torch = _torch()
     if not q.is_cuda:
         raise ValueError("q must be a GPU tensor")
@@ -261,8 +334,10 @@ def dual_head_rms_rope(q, k, qw, kw, eps: float = 1e-6, dims: int | None = None,
         raise ValueError("q [tokens, q_heads, hd] and k [tokens, k_heads, hd] expected")
     tokens, qh, hd = q.shape
     kh = k.shape[1]
-    for t, n in ((q, "q"), (k, "k"), (qw, "qw"), (kw, "kw")):
-        _require(t, n, q.dtype, q.device)
+    for t, n in ((q, "q"), (k, "k")):
+        _check_dev(t, n, q.dtype, q.device)
+    _require(qw, "qw", q.dtype, q.device)
+    _require(kw, "kw", q.dtype, q.device)
     if tuple(qw.shape) != (hd,) or tuple(kw.shape) != (hd,):
         raise ValueError("qw and kw must have shape (head_dim,)")
     dims = hd if dims is None else dims
@@ -270,13 +345,23 @@ def dual_head_rms_rope(q, k, qw, kw, eps: float = 1e-6, dims: int | None = None,
         _require(freqs, "freqs", torch.float32, q.device)
         if tuple(freqs.shape) != (dims // 2,):
             raise ValueError("freqs must have dims/2 entries")
-    qy = torch.empty_like(q) if q_out is None else q_out
-    ky = torch.empty_like(k) if k_out is None else k_out
-    _require(qy, "q_out", q.dtype, q.device)
-    _require(ky, "k_out", q.dtype, q.device)
-    _check(lib().fnorm_dual_head_rms_rope_v(
-        _ptr(q), _ptr(k), _ptr(qw), _ptr(kw), _ptr(qy), _ptr(ky), tokens, qh, kh, hd, eps, dims,
-        1 if traditional else 0, base, scale, offset, _ptr(freqs), code, _stream(q), variant))
+    qy = torch.empty(q.shape, dtype=q.dtype, device=q.device) if q_out is None else q_out
+    ky = torch.empty(k.shape, dtype=k.dtype, device=k.device) if k_out is None else k_out
+    _check_dev(qy, "q_out", q.dtype, q.device)
+    _check_dev(ky, "k_out", q.dtype, q.device)
+    if qy.shape != q.shape or ky.shape != k.shape:
+        raise ValueError("outputs must match the inputs' shapes")
+    trad = 1 if traditional else 0
+    if all(t.is_contiguous() for t in (q, k, qy, ky)):
+        _check(lib().fnorm_dual_head_rms_rope_v(
+            _ptr(q), _ptr(k), _ptr(qw), _ptr(kw), _ptr(qy), _ptr(ky), tokens, qh, kh, hd, eps,
+            dims, trad, base, scale, offset, _ptr(freqs), code, _stream(q), variant))
+    else:
+        _check(lib().fnorm_dual_head_rms_rope_strided(
+            _ptr(q), _token_stride(q, "q"), _ptr(k), _token_stride(k, "k"), _ptr(qw), _ptr(kw),
+            _ptr(qy), _token_stride(qy, "q_out"), _ptr(ky), _token_stride(ky, "k_out"), tokens,
+            qh, kh, hd, eps, dims, trad, base, scale, offset, _ptr(freqs), code, _stream(q),
+            variant))
     return qy, ky
 
 

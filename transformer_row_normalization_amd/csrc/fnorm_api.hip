@@ -273,90 +273,135 @@ int launch(const char* op, const Choice& c, NormArgs& a, void* stream) {
     return ok();
 }
 
-}  // namespace
-}  // namespace fnorm
 
-using namespace fnorm;
+// A strided tensor in memory: `count` blocks of `len` bytes, the block i
+// starting at base + i * stride bytes (one block per token or row).
+struct Span {
+    const void* base;
+    int64_t stride, len, count;
+};
 
-extern "C" {
+Span span(const void* p, int64_t stride_elems, int64_t len_elems, int64_t count, int64_t eb) {
+    return Span{p, stride_elems * eb, len_elems * eb, count};
+}
 
-int fnorm_rms_v(const void* x, const void* w, void* y, int64_t rows, int64_t width, float eps,
-                int dtype, void* stream, int variant) {
-    static const char* op = "fnorm_rms";
+// Whether two strided tensors share a byte.  Exact for two tensors with the
+// same stride whose blocks interleave (e.g. the q and k parts of one packed
+// QKV buffer); otherwise it compares the overall extents (conservative).
+bool spans_overlap(const Span& a, const Span& b) {
+    if (!a.base || !b.base || a.count <= 0 || b.count <= 0 || a.len <= 0 || b.len <= 0)
+        return false;
+    const int64_t a0 = int64_t(reinterpret_cast<uintptr_t>(a.base));
+    const int64_t b0 = int64_t(reinterpret_cast<uintptr_t>(b.base));
+    const int64_t a1 = a0 + (a.count - 1) * a.stride + a.len;
+    const int64_t b1 = b0 + (b.count - 1) * b.stride + b.len;
+    if (a1 <= b0 || b1 <= a0) return false;
+    if (a.stride == b.stride && a.stride > 0 && a.len + b.len <= a.stride) {
+        const int64_t s = a.stride;
+        const int64_t dm = (((b0 - a0) % s) + s) % s;
+        if (dm >= a.len && dm + b.len <= s) return false;
+    }
+    return true;
+}
+
+// y may be x itself (same base and stride); any other overlap is an error.
+bool output_clashes(const Span& y, const Span& x) {
+    if (y.base == x.base && y.stride == x.stride && y.len == x.len) return false;
+    return spans_overlap(y, x);
+}
+
+bool stride_aligned(int64_t stride_elems, int64_t eb) { return (stride_elems * eb) % 16 == 0; }
+
+// RMSNorm / LayerNorm over rows addressed with row strides (elements).
+int rows_impl(const char* op, bool layer, const void* x, int64_t xs, const void* w,
+              const void* b, void* y, int64_t ys, int64_t rows, int64_t width, float eps,
+              int dtype, void* stream, int variant) {
     if (int s = check_scalars(op, dtype, rows, width, eps)) return s;
+    if (rows > 1 && (xs < width || ys < width))
+        return fail(FNORM_ERR_SHAPE, op, "row strides (%lld, %lld) below width %lld",
+                    (long long)xs, (long long)ys, (long long)width);
+    if (rows > 1 && (xs > (INT64_MAX / 8) / rows || ys > (INT64_MAX / 8) / rows))
+        return fail(FNORM_ERR_SHAPE, op, "row strides overflow");
     if (rows == 0) return ok();
     if (!x || !w || !y) return fail(FNORM_ERR_NULL, op, "x, w and y must be non-NULL");
     const int64_t eb = elem_bytes(dtype);
-    const int64_t xb = rows * width * eb;
-    if (y != x && overlap(y, xb, x, xb))
-        return fail(FNORM_ERR_ALIAS, op, "y overlaps x without being equal to it");
-    if (overlap(y, xb, w, width * eb)) return fail(FNORM_ERR_ALIAS, op, "y overlaps w");
+    const Span sx = span(x, xs, width, rows, eb), sy = span(y, ys, width, rows, eb);
+    const Span sw = span(w, width, width, 1, eb), sb = span(b, width, width, 1, eb);
+    if (output_clashes(sy, sx))
+        return fail(FNORM_ERR_ALIAS, op, "y overlaps x without being x itself");
+    if (spans_overlap(sy, sw)) return fail(FNORM_ERR_ALIAS, op, "y overlaps w");
+    if (spans_overlap(sy, sb)) return fail(FNORM_ERR_ALIAS, op, "y overlaps b");
+    const bool al = aligned16(x) && aligned16(w) && aligned16(y) && (!b || aligned16(b)) &&
+                    (rows == 1 || (stride_aligned(xs, eb) && stride_aligned(ys, eb)));
     Choice c;
-    const bool al = aligned16(x) && aligned16(w) && aligned16(y);
-    if (!pick(K_RMS, dtype, width, al, variant, &c))
+    const int kind = layer ? op_kind(FNORM_OP_LAYER, b != nullptr) : K_RMS;
+    if (!pick(kind, dtype, width, al, variant, &c))
         return fail(FNORM_ERR_UNSUPPORTED, op, "no kernel variant %d for width %lld", variant,
                     (long long)width);
-    NormArgs a{x, w, nullptr, y, nullptr, nullptr, nullptr, rows, rows, width, eps};
+    NormArgs a{x,    w,    b,     y,     nullptr, nullptr, nullptr, rows, rows, width,
+               eps,  rows == 1 ? width : xs, rows == 1 ? width : ys, 1, width, width, 1};
     return launch(op, c, a, stream);
 }
 
-int fnorm_rms(const void* x, const void* w, void* y, int64_t rows, int64_t width, float eps,
-              int dtype, void* stream) {
-    return fnorm_rms_v(x, w, y, rows, width, eps, dtype, stream, -1);
-}
-
-int fnorm_layer_v(const void* x, const void* w, const void* b, void* y, int64_t rows,
-                  int64_t width, float eps, int dtype, void* stream, int variant) {
-    static const char* op = "fnorm_layer";
-    if (int s = check_scalars(op, dtype, rows, width, eps)) return s;
-    if (rows == 0) return ok();
-    if (!x || !w || !y) return fail(FNORM_ERR_NULL, op, "x, w and y must be non-NULL");
-    const int64_t eb = elem_bytes(dtype);
-    const int64_t xb = rows * width * eb;
-    if (y != x && overlap(y, xb, x, xb))
-        return fail(FNORM_ERR_ALIAS, op, "y overlaps x without being equal to it");
-    if (overlap(y, xb, w, width * eb)) return fail(FNORM_ERR_ALIAS, op, "y overlaps w");
-    if (overlap(y, xb, b, width * eb)) return fail(FNORM_ERR_ALIAS, op, "y overlaps b");
-    Choice c;
-    const bool al = aligned16(x) && aligned16(w) && aligned16(y) && (!b || aligned16(b));
-    if (!pick(op_kind(FNORM_OP_LAYER, b != nullptr), dtype, width, al, variant, &c))
-        return fail(FNORM_ERR_UNSUPPORTED, op, "no kernel variant %d for width %lld", variant,
-                    (long long)width);
-    NormArgs a{x, w, b, y, nullptr, nullptr, nullptr, rows, rows, width, eps};
-    return launch(op, c, a, stream);
-}
-
-int fnorm_layer(const void* x, const void* w, const void* b, void* y, int64_t rows,
-                int64_t width, float eps, int dtype, void* stream) {
-    return fnorm_layer_v(x, w, b, y, rows, width, eps, dtype, stream, -1);
-}
-
-int fnorm_dual_head_rms_v(const void* q, const void* k, const void* qw, const void* kw, void* qy,
-                          void* ky, int64_t q_rows, int64_t k_rows, int64_t head_dim, float eps,
-                          int dtype, void* stream, int variant) {
-    static const char* op = "fnorm_dual_head_rms";
-    if (int s = check_scalars(op, dtype, q_rows < k_rows ? q_rows : k_rows, head_dim, eps))
-        return s;
-    if (q_rows > INT64_MAX / 16 - k_rows ||
-        (q_rows + k_rows > 0 && head_dim > (INT64_MAX / 8) / (q_rows + k_rows)))
-        return fail(FNORM_ERR_SHAPE, op, "q_rows + k_rows overflows");
-    if (q_rows + k_rows == 0) return ok();
+// Checks shared by the dual forms: q [tokens, q_heads, hd] and k [tokens,
+// k_heads, hd] with token strides (elements) qs, ks, qys, kys.
+int dual_checks(const char* op, const void* q, int64_t qs, const void* k, int64_t ks,
+                const void* qw, const void* kw, const void* qy, int64_t qys, const void* ky,
+                int64_t kys, int64_t tokens, int64_t q_heads, int64_t k_heads, int64_t head_dim,
+                float eps, int dtype, const void* freqs, int64_t freq_count, bool* aligned) {
+    if (tokens < 0 || q_heads < 0 || k_heads < 0)
+        return fail(FNORM_ERR_SHAPE, op, "tokens=%lld q_heads=%lld k_heads=%lld must be >= 0",
+                    (long long)tokens, (long long)q_heads, (long long)k_heads);
+    if (q_heads > INT64_MAX / 4 - k_heads ||
+        (tokens > 0 && (q_heads + k_heads) > (INT64_MAX / 16) / tokens))
+        return fail(FNORM_ERR_SHAPE, op, "tokens * heads overflows");
+    if (int s = check_scalars(op, dtype, tokens * (q_heads + k_heads), head_dim, eps)) return s;
+    const int64_t qext = q_heads * head_dim, kext = k_heads * head_dim;
+    if (tokens > 1 && ((q_heads > 0 && (qs < qext || qys < qext)) ||
+                       (k_heads > 0 && (ks < kext || kys < kext))))
+        return fail(FNORM_ERR_SHAPE, op, "token strides below heads * head_dim");
+    if (tokens > 1 && (qs > (INT64_MAX / 8) / tokens || ks > (INT64_MAX / 8) / tokens ||
+                       qys > (INT64_MAX / 8) / tokens || kys > (INT64_MAX / 8) / tokens))
+        return fail(FNORM_ERR_SHAPE, op, "token strides overflow");
+    const int64_t q_rows = tokens * q_heads, k_rows = tokens * k_heads;
+    if (q_rows + k_rows == 0) return FNORM_OK;
     if (q_rows > 0 && (!q || !qw || !qy))
-        return fail(FNORM_ERR_NULL, op, "q, qw and qy must be non-NULL when q_rows > 0");
+        return fail(FNORM_ERR_NULL, op, "q, qw and qy must be non-NULL when q rows exist");
     if (k_rows > 0 && (!k || !kw || !ky))
-        return fail(FNORM_ERR_NULL, op, "k, kw and ky must be non-NULL when k_rows > 0");
+        return fail(FNORM_ERR_NULL, op, "k, kw and ky must be non-NULL when k rows exist");
     const int64_t eb = elem_bytes(dtype);
-    const int64_t qb = q_rows * head_dim * eb, kb = k_rows * head_dim * eb, wb = head_dim * eb;
-    if (qy != q && overlap(qy, qb, q, qb)) return fail(FNORM_ERR_ALIAS, op, "qy overlaps q");
-    if (ky != k && overlap(ky, kb, k, kb)) return fail(FNORM_ERR_ALIAS, op, "ky overlaps k");
-    if (overlap(qy, qb, k, kb) || overlap(ky, kb, q, qb))
+    const int64_t nq = q_rows > 0 ? tokens : 0, nk = k_rows > 0 ? tokens : 0;
+    const Span sq = span(q, qs, qext, nq, eb), sk = span(k, ks, kext, nk, eb);
+    const Span sqy = span(qy, qys, qext, nq, eb), sky = span(ky, kys, kext, nk, eb);
+    const Span sqw = span(qw, head_dim, head_dim, q_rows > 0 ? 1 : 0, eb);
+    const Span skw = span(kw, head_dim, head_dim, k_rows > 0 ? 1 : 0, eb);
+    const Span sfr = span(freqs, freq_count, freq_count, freqs ? 1 : 0, 4);
+    if (output_clashes(sqy, sq)) return fail(FNORM_ERR_ALIAS, op, "qy overlaps q");
+    if (output_clashes(sky, sk)) return fail(FNORM_ERR_ALIAS, op, "ky overlaps k");
+    if (spans_overlap(sqy, sk) || spans_overlap(sky, sq))
         return fail(FNORM_ERR_ALIAS, op, "an output overlaps the other tensor's input");
-    if (overlap(qy, qb, ky, kb)) return fail(FNORM_ERR_ALIAS, op, "qy overlaps ky");
-    if (overlap(qy, qb, qw, q_rows > 0 ? wb : 0) || overlap(qy, qb, kw, k_rows > 0 ? wb : 0) ||
-        overlap(ky, kb, qw, q_rows > 0 ? wb : 0) || overlap(ky, kb, kw, k_rows > 0 ? wb : 0))
-        return fail(FNORM_ERR_ALIAS, op, "an output overlaps a weight");
-    const bool al = (q_rows == 0 || (aligned16(q) && aligned16(qw) && aligned16(qy))) &&
-                    (k_rows == 0 || (aligned16(k) && aligned16(kw) && aligned16(ky)));
+    if (spans_overlap(sqy, sky)) return fail(FNORM_ERR_ALIAS, op, "qy overlaps ky");
+    if (spans_overlap(sqy, sqw) || spans_overlap(sqy, skw) || spans_overlap(sky, sqw) ||
+        spans_overlap(sky, skw) || spans_overlap(sqy, sfr) || spans_overlap(sky, sfr))
+        return fail(FNORM_ERR_ALIAS, op, "an output overlaps a weight or the frequency table");
+    const bool one = tokens == 1;
+    *aligned = (q_rows == 0 || (aligned16(q) && aligned16(qw) && aligned16(qy) &&
+                                (one || (stride_aligned(qs, eb) && stride_aligned(qys, eb))))) &&
+               (k_rows == 0 || (aligned16(k) && aligned16(kw) && aligned16(ky) &&
+                                (one || (stride_aligned(ks, eb) && stride_aligned(kys, eb)))));
+    return FNORM_OK;
+}
+
+int dual_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t ks,
+              const void* qw, const void* kw, void* qy, int64_t qys, void* ky, int64_t kys,
+              int64_t tokens, int64_t q_heads, int64_t k_heads, int64_t head_dim, float eps,
+              int dtype, void* stream, int variant) {
+    bool al = false;
+    if (int s = dual_checks(op, q, qs, k, ks, qw, kw, qy, qys, ky, kys, tokens, q_heads, k_heads,
+                            head_dim, eps, dtype, nullptr, 0, &al))
+        return s;
+    const int64_t q_rows = tokens * q_heads, k_rows = tokens * k_heads;
+    if (q_rows + k_rows == 0) return ok();
     Choice c;
     if (!pick(K_DUAL, dtype, head_dim, al, variant, &c))
         return fail(FNORM_ERR_UNSUPPORTED, op, "no kernel variant %d for head_dim %lld", variant,
@@ -365,55 +410,33 @@ int fnorm_dual_head_rms_v(const void* q, const void* k, const void* qw, const vo
     // valid weight pointer so its register preload stays in bounds.
     const void* qw_eff = q_rows > 0 ? qw : kw;
     const void* kw_eff = k_rows > 0 ? kw : qw;
-    NormArgs a{q, qw_eff, nullptr, qy, k, kw_eff, ky, q_rows + k_rows, q_rows, head_dim, eps};
+    // One-token tensors, and tokens packed back to back, address as plain rows.
+    const bool qplain = tokens == 1 || (qs == q_heads * head_dim && qys == qs);
+    const bool kplain = tokens == 1 || (ks == k_heads * head_dim && kys == ks);
+    NormArgs a{q, qw_eff, nullptr, qy, k, kw_eff, ky, q_rows + k_rows, q_rows, head_dim, eps,
+               qplain ? head_dim : qs, qplain ? head_dim : qys, qplain ? 1 : q_heads,
+               kplain ? head_dim : ks, kplain ? head_dim : kys, kplain ? 1 : k_heads};
     return launch(op, c, a, stream);
 }
 
-int fnorm_dual_head_rms(const void* q, const void* k, const void* qw, const void* kw, void* qy,
-                        void* ky, int64_t q_rows, int64_t k_rows, int64_t head_dim, float eps,
-                        int dtype, void* stream) {
-    return fnorm_dual_head_rms_v(q, k, qw, kw, qy, ky, q_rows, k_rows, head_dim, eps, dtype,
-                                 stream, -1);
-}
-
-int fnorm_dual_head_rms_rope_v(const void* q, const void* k, const void* qw, const void* kw,
-                               void* qy, void* ky, int64_t tokens, int64_t q_heads,
-                               int64_t k_heads, int64_t head_dim, float eps, int64_t rope_dims,
-                               int traditional, float base, float scale, int64_t offset,
-                               const float* freqs, int dtype, void* stream, int variant) {
-    static const char* op = "fnorm_dual_head_rms_rope";
-    if (tokens < 0 || q_heads < 0 || k_heads < 0)
-        return fail(FNORM_ERR_SHAPE, op, "tokens=%lld q_heads=%lld k_heads=%lld must be >= 0",
-                    (long long)tokens, (long long)q_heads, (long long)k_heads);
-    if (q_heads > (int64_t(1) << 30) || k_heads > (int64_t(1) << 30) ||
-        (tokens > 0 && (q_heads + k_heads) > (INT64_MAX / 16) / tokens))
-        return fail(FNORM_ERR_SHAPE, op, "tokens * heads overflows");
-    const int64_t q_rows = tokens * q_heads, k_rows = tokens * k_heads;
-    if (int s = check_scalars(op, dtype, q_rows + k_rows, head_dim, eps)) return s;
+int rope_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t ks,
+              const void* qw, const void* kw, void* qy, int64_t qys, void* ky, int64_t kys,
+              int64_t tokens, int64_t q_heads, int64_t k_heads, int64_t head_dim, float eps,
+              int64_t rope_dims, int traditional, float base, float scale, int64_t offset,
+              const float* freqs, int dtype, void* stream, int variant) {
     if (rope_dims < 2 || rope_dims % 2 != 0 || rope_dims > head_dim)
         return fail(FNORM_ERR_SHAPE, op, "rope_dims=%lld must be even and in [2, head_dim=%lld]",
                     (long long)rope_dims, (long long)head_dim);
     if (!std::isfinite(scale) || (!freqs && (!std::isfinite(base) || base <= 0.0f)))
         return fail(FNORM_ERR_SHAPE, op, "base must be finite and > 0, scale finite");
-    if (offset < 0 || offset > (int64_t(1) << 52) - tokens)
+    if (offset < 0 || tokens < 0 || offset > (int64_t(1) << 52) - tokens)
         return fail(FNORM_ERR_SHAPE, op, "offset=%lld out of range", (long long)offset);
+    bool al = false;
+    if (int s = dual_checks(op, q, qs, k, ks, qw, kw, qy, qys, ky, kys, tokens, q_heads, k_heads,
+                            head_dim, eps, dtype, freqs, rope_dims / 2, &al))
+        return s;
+    const int64_t q_rows = tokens * q_heads, k_rows = tokens * k_heads;
     if (q_rows + k_rows == 0) return ok();
-    if (q_rows > 0 && (!q || !qw || !qy))
-        return fail(FNORM_ERR_NULL, op, "q, qw and qy must be non-NULL when q rows exist");
-    if (k_rows > 0 && (!k || !kw || !ky))
-        return fail(FNORM_ERR_NULL, op, "k, kw and ky must be non-NULL when k rows exist");
-    const int64_t eb = elem_bytes(dtype);
-    const int64_t qb = q_rows * head_dim * eb, kb = k_rows * head_dim * eb, wb = head_dim * eb;
-    if (qy != q && overlap(qy, qb, q, qb)) return fail(FNORM_ERR_ALIAS, op, "qy overlaps q");
-    if (ky != k && overlap(ky, kb, k, kb)) return fail(FNORM_ERR_ALIAS, op, "ky overlaps k");
-    if (overlap(qy, qb, k, kb) || overlap(ky, kb, q, qb) || overlap(qy, qb, ky, kb))
-        return fail(FNORM_ERR_ALIAS, op, "an output overlaps another tensor");
-    if (overlap(qy, qb, qw, q_rows > 0 ? wb : 0) || overlap(qy, qb, kw, k_rows > 0 ? wb : 0) ||
-        overlap(ky, kb, qw, q_rows > 0 ? wb : 0) || overlap(ky, kb, kw, k_rows > 0 ? wb : 0) ||
-        overlap(qy, qb, freqs, rope_dims * 2) || overlap(ky, kb, freqs, rope_dims * 2))
-        return fail(FNORM_ERR_ALIAS, op, "an output overlaps a weight or the frequency table");
-    const bool al = (q_rows == 0 || (aligned16(q) && aligned16(qw) && aligned16(qy))) &&
-                    (k_rows == 0 || (aligned16(k) && aligned16(kw) && aligned16(ky)));
     const int kind = traditional ? K_ROPE_TRAD : K_ROPE_SPLIT;
     const Variant* list[kMaxCandidates];
     const int n = rope_candidates(kind, dtype, head_dim, al, rope_dims, list);
@@ -426,8 +449,9 @@ int fnorm_dual_head_rms_rope_v(const void* q, const void* k, const void* qw, con
     const bool persistent = variant % 2 == 0;
     const void* qw_eff = q_rows > 0 ? qw : kw;
     const void* kw_eff = k_rows > 0 ? kw : qw;
-    RopeArgs ra{NormArgs{q, qw_eff, nullptr, qy, k, kw_eff, ky, q_rows + k_rows, q_rows, head_dim,
-                         eps},
+    RopeArgs ra{NormArgs{q, qw_eff, nullptr, qy, k, kw_eff, ky, q_rows + k_rows, q_rows,
+                         head_dim, eps, qs, qys, q_heads > 0 ? q_heads : 1, ks, kys,
+                         k_heads > 0 ? k_heads : 1},
                 q_heads > 0 ? q_heads : 1, k_heads > 0 ? k_heads : 1, rope_dims, offset, base,
                 scale, freqs};
     const int64_t lds = rope_lds_bytes(*v, rope_dims);
@@ -452,6 +476,90 @@ int fnorm_dual_head_rms_rope_v(const void* q, const void* k, const void* qw, con
     return ok();
 }
 
+}  // namespace
+}  // namespace fnorm
+
+using namespace fnorm;
+
+extern "C" {
+
+int fnorm_rms_v(const void* x, const void* w, void* y, int64_t rows, int64_t width, float eps,
+                int dtype, void* stream, int variant) {
+    return rows_impl("fnorm_rms", false, x, width, w, nullptr, y, width, rows, width, eps, dtype,
+                     stream, variant);
+}
+
+int fnorm_rms(const void* x, const void* w, void* y, int64_t rows, int64_t width, float eps,
+              int dtype, void* stream) {
+    return fnorm_rms_v(x, w, y, rows, width, eps, dtype, stream, -1);
+}
+
+int fnorm_rms_strided(const void* x, int64_t x_stride, const void* w, void* y, int64_t y_stride,
+                      int64_t rows, int64_t width, float eps, int dtype, void* stream,
+                      int variant) {
+    return rows_impl("fnorm_rms_strided", false, x, x_stride, w, nullptr, y, y_stride, rows,
+                     width, eps, dtype, stream, variant);
+}
+
+int fnorm_layer_v(const void* x, const void* w, const void* b, void* y, int64_t rows,
+                  int64_t width, float eps, int dtype, void* stream, int variant) {
+    return rows_impl("fnorm_layer", true, x, width, w, b, y, width, rows, width, eps, dtype,
+                     stream, variant);
+}
+
+int fnorm_layer(const void* x, const void* w, const void* b, void* y, int64_t rows,
+                int64_t width, float eps, int dtype, void* stream) {
+    return fnorm_layer_v(x, w, b, y, rows, width, eps, dtype, stream, -1);
+}
+
+int fnorm_layer_strided(const void* x, int64_t x_stride, const void* w, const void* b, void* y,
+                        int64_t y_stride, int64_t rows, int64_t width, float eps, int dtype,
+                        void* stream, int variant) {
+    return rows_impl("fnorm_layer_strided", true, x, x_stride, w, b, y, y_stride, rows, width,
+                     eps, dtype, stream, variant);
+}
+
+int fnorm_dual_head_rms_v(const void* q, const void* k, const void* qw, const void* kw, void* qy,
+                          void* ky, int64_t q_rows, int64_t k_rows, int64_t head_dim, float eps,
+                          int dtype, void* stream, int variant) {
+    static const char* op = "fnorm_dual_head_rms";
+    if (q_rows < 0 || k_rows < 0)
+        return fail(FNORM_ERR_SHAPE, op, "q_rows=%lld k_rows=%lld must be >= 0",
+                    (long long)q_rows, (long long)k_rows);
+    // contiguous head vectors: one "token" whose heads are all the rows
+    return dual_impl(op, q, q_rows * head_dim, k, k_rows * head_dim, qw, kw, qy,
+                     q_rows * head_dim, ky, k_rows * head_dim, 1, q_rows, k_rows, head_dim, eps,
+                     dtype, stream, variant);
+}
+
+int fnorm_dual_head_rms(const void* q, const void* k, const void* qw, const void* kw, void* qy,
+                        void* ky, int64_t q_rows, int64_t k_rows, int64_t head_dim, float eps,
+                        int dtype, void* stream) {
+    return fnorm_dual_head_rms_v(q, k, qw, kw, qy, ky, q_rows, k_rows, head_dim, eps, dtype,
+                                 stream, -1);
+}
+
+int fnorm_dual_head_rms_strided(const void* q, int64_t q_stride, const void* k,
+                                int64_t k_stride, const void* qw, const void* kw, void* qy,
+                                int64_t qy_stride, void* ky, int64_t ky_stride, int64_t tokens,
+                                int64_t q_heads, int64_t k_heads, int64_t head_dim, float eps,
+                                int dtype, void* stream, int variant) {
+    return dual_impl("fnorm_dual_head_rms_strided", q, q_stride, k, k_stride, qw, kw, qy,
+                     qy_stride, ky, ky_stride, tokens, q_heads, k_heads, head_dim, eps, dtype,
+                     stream, variant);
+}
+
+int fnorm_dual_head_rms_rope_v(const void* q, const void* k, const void* qw, const void* kw,
+                               void* qy, void* ky, int64_t tokens, int64_t q_heads,
+                               int64_t k_heads, int64_t head_dim, float eps, int64_t rope_dims,
+                               int traditional, float base, float scale, int64_t offset,
+                               const float* freqs, int dtype, void* stream, int variant) {
+    return rope_impl("fnorm_dual_head_rms_rope", q, q_heads * head_dim, k, k_heads * head_dim,
+                     qw, kw, qy, q_heads * head_dim, ky, k_heads * head_dim, tokens, q_heads,
+                     k_heads, head_dim, eps, rope_dims, traditional, base, scale, offset, freqs,
+                     dtype, stream, variant);
+}
+
 int fnorm_dual_head_rms_rope(const void* q, const void* k, const void* qw, const void* kw,
                              void* qy, void* ky, int64_t tokens, int64_t q_heads,
                              int64_t k_heads, int64_t head_dim, float eps, int64_t rope_dims,
@@ -460,6 +568,18 @@ int fnorm_dual_head_rms_rope(const void* q, const void* k, const void* qw, const
     return fnorm_dual_head_rms_rope_v(q, k, qw, kw, qy, ky, tokens, q_heads, k_heads, head_dim,
                                       eps, rope_dims, traditional, base, scale, offset, freqs,
                                       dtype, stream, -1);
+}
+
+int fnorm_dual_head_rms_rope_strided(const void* q, int64_t q_stride, const void* k,
+                                     int64_t k_stride, const void* qw, const void* kw, void* qy,
+                                     int64_t qy_stride, void* ky, int64_t ky_stride,
+                                     int64_t tokens, int64_t q_heads, int64_t k_heads,
+                                     int64_t head_dim, float eps, int64_t rope_dims,
+                                     int traditional, float base, float scale, int64_t offset,
+                                     const float* freqs, int dtype, void* stream, int variant) {
+    return rope_impl("fnorm_dual_head_rms_rope_strided", q, q_stride, k, k_stride, qw, kw, qy,
+                     qy_stride, ky, ky_stride, tokens, q_heads, k_heads, head_dim, eps,
+                     rope_dims, traditional, base, scale, offset, freqs, dtype, stream, variant);
 }
 
 int fnorm_variant_count(int op, int dtype, int64_t width, int aligned) {

@@ -50,7 +50,30 @@ struct NormArgs {
     int64_t rows1;      // rows of the first tensor (== rows unless dual)
     int64_t width;
     float eps;
+    // Row addressing, in elements: row r of x starts at
+    //   (r / xh) * xs + (r % xh) * width
+    // (xh rows per token, xs the token stride; xh = 1 and xs = width for a
+    // contiguous tensor) and its output row at the same with ys.  x2 / y2
+    // likewise with x2h, x2s, y2s.
+    int64_t xs, ys, xh;
+    int64_t x2s, y2s, x2h;
 };
+
+struct RowOff {
+    int64_t x, y;
+};
+
+// Element offsets of row r's input and output (see NormArgs).  One-row
+// tokens take no division; otherwise one 32-bit division when it fits.
+__device__ __forceinline__ RowOff row_offsets(int64_t r, int64_t heads, int64_t xs, int64_t ys,
+                                              int64_t width) {
+    if (heads == 1) return RowOff{r * xs, r * ys};
+    const int64_t t = (r <= 0x7fffffff && heads <= 0x7fffffff)
+                          ? int64_t(uint32_t(r) / uint32_t(heads))
+                          : r / heads;
+    const int64_t h = r - t * heads;
+    return RowOff{t * xs + h * width, t * ys + h * width};
+}
 
 template <int OP, int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, bool BIAS,
           bool DUAL, int NT>
@@ -114,7 +137,8 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
                 r = row - a.rows1;
             }
         }
-        const int64_t row_off = r * width;
+        const RowOff off = second ? row_offsets(r, a.x2h, a.x2s, a.y2s, width)
+                                  : row_offsets(r, a.xh, a.xs, a.ys, width);
         if constexpr (PACK_W) {
             keep_packed<VPT>(wv);
             if constexpr (BIAS) keep_packed<VPT>(bv);
@@ -124,7 +148,7 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
         R xv[VPT];
 #pragma unroll
         for (int v = 0; v < VPT; ++v)
-            xv[v] = in_row(v) ? load_raw<DT, VEC, NT_LD>(xp, row_off + col_of(v))
+            xv[v] = in_row(v) ? load_raw<DT, VEC, NT_LD>(xp, off.x + col_of(v))
                               : raw_zero<DT, VEC>();
 
         // Row scalars: out = (x - shift) * scale * w + bias.
@@ -180,7 +204,7 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
                         const float bias = BIAS ? elem<DT, VEC>(bv[v], i) : 0.0f;
                         o[i] = __builtin_fmaf(d * scale, elem<DT, VEC>(wv[v], i), bias);
                     }
-                    if (in_row(v)) store_raw<DT, VEC, NT_ST>(yp, row_off + col_of(v), make_raw<DT, VEC>(o));
+                    if (in_row(v)) store_raw<DT, VEC, NT_ST>(yp, off.y + col_of(v), make_raw<DT, VEC>(o));
                 }
             }
             continue;
@@ -194,7 +218,7 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
 #pragma unroll
                 for (int i = 0; i < VEC; ++i)
                     o[i] = (elem<DT, VEC>(xv[v], i) * scale) * elem<DT, VEC>(wr, i);
-                if (in_row(v)) store_raw<DT, VEC, NT_ST>(yp, row_off + col_of(v), make_raw<DT, VEC>(o));
+                if (in_row(v)) store_raw<DT, VEC, NT_ST>(yp, off.y + col_of(v), make_raw<DT, VEC>(o));
             }
         }
     }
@@ -205,7 +229,7 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
 // BLOCK * VEC.  RMSNorm: one pass for sum(x^2), one to normalize.
 // LayerNorm: one pass for the mean, one for the squared deviations, one to
 // normalize (the same corrected two-pass as above).  The dual form is not
-// offered here.
+// offered here; rows are addressed with a plain row stride (xh = 1).
 template <int OP, int DT, int VEC, int BLOCK, bool BIAS>
 __global__ __launch_bounds__(BLOCK) void norm_rows_wide(NormArgs a) {
     using R = typename Raw<DT, VEC>::type;
@@ -216,7 +240,8 @@ __global__ __launch_bounds__(BLOCK) void norm_rows_wide(NormArgs a) {
     constexpr int64_t STEP = int64_t(BLOCK) * VEC;
 
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
-        const int64_t off = row * width;
+        const int64_t off = row * a.xs;
+        const int64_t yoff = row * a.ys;
         float s, mean = 0.0f, c = 0.0f;
         if constexpr (OP == OP_RMS) {
             float ss = 0.0f;
@@ -270,7 +295,7 @@ __global__ __launch_bounds__(BLOCK) void norm_rows_wide(NormArgs a) {
                     o[i] = __builtin_fmaf(d * s, elem<DT, VEC>(wr, i), elem<DT, VEC>(br, i));
                 }
             }
-            store_raw<DT, VEC, false>(a.y, off + col, make_raw<DT, VEC>(o));
+            store_raw<DT, VEC, false>(a.y, yoff + col, make_raw<DT, VEC>(o));
         }
         // The partial slots of this row are read above; make sure every wave
         // is past those reads before the next row overwrites them.
@@ -333,7 +358,8 @@ namespace fnorm {
 // neighbouring lane for scalar packs).  The host only launches shapes for
 // which one of these holds.
 struct RopeArgs {
-    NormArgs n;          // x = q, w = qw, y = qy, x2 = k, w2 = kw, y2 = ky
+    NormArgs n;          // x = q, w = qw, y = qy, x2 = k, w2 = kw, y2 = ky; xs / ys /
+                         // x2s / y2s are token strides (heads taken from below)
     int64_t q_heads;     // >= 1 (1 when there are no query rows)
     int64_t k_heads;     // >= 1 (1 when there are no key rows)
     int64_t dims;        // rotated features, even, <= width
@@ -398,18 +424,21 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
         const bool second = row >= a.rows1;
         const void* xp = second ? a.x2 : a.x;
         void* yp = second ? a.y2 : a.y;
-        const int64_t row_off = (second ? row - a.rows1 : row) * width;
-        R xv[VPT];
-#pragma unroll
-        for (int v = 0; v < VPT; ++v)
-            xv[v] = in_row(v) ? load_raw<DT, VEC, NT_LD>(xp, row_off + col_of(v))
-                              : raw_zero<DT, VEC>();
-
-        // Token of this row, its position, and the first slot of this
-        // wavefront holding the same token (the slot that owns the table).
+        // token of this row (heads of a token are consecutive rows)
         const int64_t num = second ? row - a.rows1 : row;
         const int64_t den = second ? ra.k_heads : ra.q_heads;
         const int64_t tok = small ? int64_t(uint32_t(num) / uint32_t(den)) : num / den;
+        const int64_t head = num - tok * den;
+        const int64_t xo = tok * (second ? a.x2s : a.xs) + head * width;
+        const int64_t yo = tok * (second ? a.y2s : a.ys) + head * width;
+        R xv[VPT];
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+            xv[v] = in_row(v) ? load_raw<DT, VEC, NT_LD>(xp, xo + col_of(v))
+                              : raw_zero<DT, VEC>();
+
+        // Its position, and the first slot of this wavefront holding the
+        // same token (the slot that owns the table).
         const int64_t first = (second ? a.rows1 : 0) + tok * den;
         const int64_t wave_row0 = base + int64_t(wave) * W;
         const int leader = first > wave_row0 ? int(first - wave_row0) : 0;
@@ -555,7 +584,7 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
 #pragma unroll
             for (int v = 0; v < VPT; ++v)
                 if (in_row(v))
-                    store_raw<DT, VEC, NT_ST>(yp, row_off + col_of(v), make_raw<DT, VEC>(out[v]));
+                    store_raw<DT, VEC, NT_ST>(yp, yo + col_of(v), make_raw<DT, VEC>(out[v]));
         }
         // every lane has read the table before the next block-row rewrites it
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
