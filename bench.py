@@ -17,8 +17,10 @@ caches: 1.6 GB of other traffic separates two reads of the same tensor, more
 than the 256 MB MALL.
 
 Prints ONE JSON line.  Extra legs (outside the timed region): the plain
-copy kernel over the LayerNorm's bytes (practical ceiling) and the fp64 CPU
-oracle over full steps for about 10 s (``cpu_baseline``).
+copy kernel over the LayerNorm's bytes (practical ceiling), fused against
+composed (ABBA), the dual launch with RoPE fused in, decode-sized calls
+(eager and HIP-graph replay), and the fp64 CPU oracle over full steps for
+about 10 s (``cpu_baseline``).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -190,9 +192,11 @@ def main():
 
     composed = None
     rope = None
+    decode = None
     if not args.no_composed and len(plan) == 3:
         composed = fused_vs_composed(trn, inputs, dev, stream, d, wl_rms, wl_ln, log)
         rope = dual_rope_leg(trn, dq, qy, ky, wl_dual.eps, stream, log)
+        decode = decode_leg(trn, dev, stream, log)
 
     cpu = None
     if not args.no_cpu_baseline and len(plan) == 3:
@@ -211,7 +215,7 @@ def main():
                       "parallelism": "rows across workgroups (1 GPU)"},
            "per_op": per_op, "copy_ceiling": ceiling,
            "roofline": roofline, "cpu_baseline": cpu, "fused_vs_composed": composed,
-           "dual_rope": rope,
+           "dual_rope": rope, "decode": decode,
            "wall_s_timed_region": round(wall, 4)}
     print(json.dumps(out), flush=True)
 
@@ -292,6 +296,70 @@ def dual_rope_leg(trn, dq, qy, ky, eps, stream, log):
                "gbs_min": round(nbytes / (min(v) * 1e-6) / 1e9, 1)} for k, v in times.items()}
     out["kernel"] = trn.describe_rope(trn.BF16, 128, 128, False)
     log(f"[bench] dual + rope: {out}")
+    return out
+
+
+def decode_leg(trn, dev, stream, log):
+    """Decode-sized calls, where launches dominate: one decode step of the
+    dual workload's head layout (32 query heads, 8 key heads, head_dim 128,
+    bf16) at 1, 8 and 64 tokens.  Arms per layer: two single RMSNorm
+    launches (q, then k), the one dual launch, and the dual launch with RoPE
+    (position 1000 + token).  Timed two ways, ABBA over the arms:
+      eager  - 200 back-to-back calls between two events: what a host loop
+               sustains, launch submission included;
+      graph  - one HIP graph holding 64 calls, replayed 10 times: device
+               time per call with the host out of the loop."""
+    import torch
+
+    g = torch.Generator().manual_seed(5)
+    qh, kh, hd = 32, 8, 128
+    out = {}
+    for tokens in (1, 8, 64):
+        q = torch.randn(tokens, qh, hd, generator=g).to(torch.bfloat16).to(dev)
+        k = torch.randn(tokens, kh, hd, generator=g).to(torch.bfloat16).to(dev)
+        qw = (1 + 0.1 * torch.randn(hd, generator=g)).to(torch.bfloat16).to(dev)
+        kw = (1 + 0.1 * torch.randn(hd, generator=g)).to(torch.bfloat16).to(dev)
+        qy, ky = torch.empty_like(q), torch.empty_like(k)
+        arms = {
+            "two_rms": lambda: (trn.rms_norm(q, qw, 1e-6, out=qy), trn.rms_norm(k, kw, 1e-6, out=ky)),
+            "dual": lambda: trn.dual_head_rms_norm(q, k, qw, kw, 1e-6, q_out=qy, k_out=ky),
+            "dual_rope": lambda: trn.dual_head_rms_rope(q, k, qw, kw, 1e-6, offset=1000,
+                                                        q_out=qy, k_out=ky)}
+        graphs = {}
+        for name, f in arms.items():
+            for _ in range(3):
+                f()
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for _ in range(64):
+                    f()
+            graphs[name] = gr
+        times = {n: {"eager": [], "graph": []} for n in arms}
+        for r in range(6):
+            order = list(arms) if r % 2 == 0 else list(arms)[::-1]
+            for name in order:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for _ in range(200):
+                    arms[name]()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times[name]["eager"].append(e0.elapsed_time(e1) * 1e3 / 200)
+                graphs[name].replay()
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for _ in range(10):
+                    graphs[name].replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times[name]["graph"].append(e0.elapsed_time(e1) * 1e3 / 640)
+        rec = {n: {m: round(min(v), 2) for m, v in t.items()} for n, t in times.items()}
+        rec["unit"] = "us per call (min over 6 ABBA reps)"
+        out[f"tokens_{tokens}"] = rec
+        log(f"[bench] decode tokens={tokens}: {rec}")
+        del graphs
     return out
 
 

@@ -13,6 +13,8 @@
 #include <cstdio>
 #include <cstring>
 #include <memory>
+#include <mutex>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/fnorm.h"
@@ -252,6 +254,24 @@ int blocks_per_cu(const Variant* v) {
     return n;
 }
 
+// Resident workgroups per CU of a variant launched with `lds` bytes of
+// dynamic LDS, cached so that repeated calls (and calls recorded into a HIP
+// graph) make no occupancy query.
+int blocks_per_cu_lds(const Variant* v, int64_t lds) {
+    static std::mutex mu;
+    static std::unordered_map<uint64_t, int> cache;
+    const uint64_t key = (uint64_t(v - registry().table.data()) << 32) | uint64_t(lds);
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, v->fn, v->block, size_t(lds)) !=
+            hipSuccess || n <= 0)
+        n = 1;
+    cache.emplace(key, n);
+    return n;
+}
+
 int launch(const char* op, const Choice& c, NormArgs& a, void* stream) {
     const int64_t rpb = c.v->rows_per_block();
     const int64_t needed = (a.rows + rpb - 1) / rpb;
@@ -458,10 +478,7 @@ int rope_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
     const int64_t rpb = v->rows_per_block();
     int64_t grid = (ra.n.rows + rpb - 1) / rpb;
     if (persistent) {
-        int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, v->fn, v->block, size_t(lds)) !=
-                hipSuccess || per_cu <= 0)
-            per_cu = 1;
+        const int per_cu = blocks_per_cu_lds(v, lds);
         const int64_t cap = int64_t(device_cus()) * per_cu;
         if (grid > cap) grid = cap;
     }
