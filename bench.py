@@ -156,25 +156,33 @@ def main():
     step_rows = sum(p[3] for p in plan)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # practical ceiling: 16-byte copy kernel over the LayerNorm's byte count
-    ceiling = None
-    if "layer" in ops:
-        n = dln["x"].numel()
-        src, dst = dln["x"], y_ln
+    # practical ceiling: the 16-byte copy kernel moving the same bytes as the
+    # LayerNorm (the dominant kernel) and as the dual launch (small enough
+    # that the launch's ramp-up and tail show)
+    def copy_ceiling(nbytes_each_way):
+        src = dln["x"].view(-1).view(torch.uint8)[:nbytes_each_way]
+        dst = y_ln.view(-1).view(torch.uint8)[:nbytes_each_way]
         for _ in range(3):
             trn.bench_copy(src, dst)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 10
+        reps = 20
         e0.record(stream)
         for _ in range(reps):
             trn.bench_copy(src, dst)
         e1.record(stream)
         torch.cuda.synchronize()
         cms = e0.elapsed_time(e1) / reps
-        ceiling = {"kernel": "copy16 (fnorm_bench_copy)", "bytes": 2 * n * 2,
-                   "avg_ms": round(cms, 5),
-                   "gbs": round(2 * n * 2 / (cms * 1e-3) / 1e9, 1)}
+        return {"kernel": "copy16 (fnorm_bench_copy)", "bytes": 2 * nbytes_each_way,
+                "avg_ms": round(cms, 5),
+                "gbs": round(2 * nbytes_each_way / (cms * 1e-3) / 1e9, 1)}
+
+    ceiling = None
+    if "layer" in ops:
+        ceiling = copy_ceiling(dln["x"].numel() * dln["x"].element_size())
+        if "dual" in ops:
+            qk = nbytes(dq["q"], dq["k"])
+            ceiling["at_dual_bytes"] = copy_ceiling(qk - qk % 16)
         log(f"[bench] copy ceiling: {ceiling}")
 
     dominant = max(per_op, key=lambda k: per_op[k]["avg_ms"])

@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace fnorm {
 
 enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
@@ -60,6 +62,19 @@ __device__ __forceinline__ typename Raw<DT, VEC>::type load_raw(const void* base
                                             idx * Elem<DT>::bytes);
     if constexpr (NT) return __builtin_nontemporal_load(p);
     else return *p;
+}
+
+// f(0), f(1), ..., f(N-1) with compile-time indices and no loop in the IR.
+// Used for the row stores: a `#pragma unroll` loop of one trip is still a
+// loop when LICM runs, and its store promotion re-creates the store without
+// the !nontemporal metadata.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 template <int DT, int VEC, bool NT>

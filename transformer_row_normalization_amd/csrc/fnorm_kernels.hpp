@@ -118,41 +118,56 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
             wv2[v] = in_row(v) ? load_raw<DT, VEC, false>(a.w2, col_of(v)) : raw_zero<DT, VEC>();
     }
 
-    int parity = 0;
-    for (int64_t base = int64_t(blockIdx.x) * RPB; base < a.rows;
-         base += int64_t(gridDim.x) * RPB) {
-        // Row groups past the end re-read the last row (in bounds, so the
-        // loads need no predicate) and store nothing.
-        const bool valid = base + group <= last;
-        const int64_t row = valid ? base + group : last;
-        const void* xp = a.x;
-        void* yp = a.y;
+    // Where block-row `base` of this thread's row group lives.  Row groups
+    // past the end re-read the last row (in bounds, so the loads need no
+    // predicate) and store nothing.  (Issuing the next block-row's loads
+    // before this row's reductions measured slower on every bench shape.)
+    struct Loc {
+        bool valid, second;
+        const void* xp;
+        void* yp;
+        RowOff off;
+    };
+    auto locate = [&](int64_t base) {
+        Loc L;
+        L.valid = base + group <= last;
+        const int64_t row = L.valid ? base + group : last;
+        L.xp = a.x;
+        L.yp = a.y;
+        L.second = false;
         int64_t r = row;
-        bool second = false;
         if constexpr (DUAL) {
-            second = row >= a.rows1;
-            if (second) {
-                xp = a.x2;
-                yp = a.y2;
+            L.second = row >= a.rows1;
+            if (L.second) {
+                L.xp = a.x2;
+                L.yp = a.y2;
                 r = row - a.rows1;
             }
         }
-        const RowOff off = second ? row_offsets(r, a.x2h, a.x2s, a.y2s, width)
-                                  : row_offsets(r, a.xh, a.xs, a.ys, width);
+        L.off = L.second ? row_offsets(r, a.x2h, a.x2s, a.y2s, width)
+                         : row_offsets(r, a.xh, a.xs, a.ys, width);
+        return L;
+    };
+    auto load_row = [&](const Loc& L, R* dst) {
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+            dst[v] = in_row(v) ? load_raw<DT, VEC, NT_LD>(L.xp, L.off.x + col_of(v))
+                               : raw_zero<DT, VEC>();
+    };
+
+    int parity = 0;
+    for (int64_t base = int64_t(blockIdx.x) * RPB; base < a.rows;
+         base += int64_t(gridDim.x) * RPB) {
+        const Loc cur = locate(base);
+        R xv[VPT];
+        load_row(cur, xv);
         if constexpr (PACK_W) {
             keep_packed<VPT>(wv);
             if constexpr (BIAS) keep_packed<VPT>(bv);
             if constexpr (DUAL) keep_packed<VPT>(wv2);
         }
 
-        R xv[VPT];
-#pragma unroll
-        for (int v = 0; v < VPT; ++v)
-            xv[v] = in_row(v) ? load_raw<DT, VEC, NT_LD>(xp, off.x + col_of(v))
-                              : raw_zero<DT, VEC>();
-
-        // Row scalars: out = (x - shift) * scale * w + bias.
-        float shift = 0.0f, scale;
+        // Row scalars, then out = (x - shift) * scale * w + bias.
         if constexpr (OP == OP_RMS) {
             float ss = 0.0f;
 #pragma unroll
@@ -164,8 +179,29 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
                 }
             ss = row_sum<LPR>(ss, red[parity], group, lane);
             parity ^= 1;
-            scale = __builtin_amdgcn_rsqf(ss / fwidth + a.eps);
+            const float scale = __builtin_amdgcn_rsqf(ss / fwidth + a.eps);
             if constexpr (PACK_X) keep_packed<VPT>(xv);
+            if (cur.valid) {
+                static_for<VPT>([&](auto vi) {
+                    constexpr int v = decltype(vi)::value;
+                    // a select of values: selecting between the two arrays'
+                    // elements as lvalues makes a pointer select, which can
+                    // push both weight arrays to scratch memory
+                    const R w1 = wv[v];
+                    R wr = w1;
+                    if constexpr (DUAL) {
+                        const R w2 = wv2[v];
+                        wr = cur.second ? w2 : w1;
+                    }
+                    float o[VEC];
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i)
+                        o[i] = (elem<DT, VEC>(xv[v], i) * scale) * elem<DT, VEC>(wr, i);
+                    if (in_row(v))
+                        store_raw<DT, VEC, NT_ST>(cur.yp, cur.off.y + col_of(v),
+                                                  make_raw<DT, VEC>(o));
+                });
+            }
         } else {
             float sum = 0.0f;
 #pragma unroll
@@ -190,35 +226,23 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
             row_sum2<LPR>(sd, sq, red[1], red[2], group, lane);
             const float c = sd / fwidth;
             const float var = __builtin_fmaxf((sq - c * sd) / fwidth, 0.0f);
-            scale = __builtin_amdgcn_rsqf(var + a.eps);
-            shift = mean;
+            const float scale = __builtin_amdgcn_rsqf(var + a.eps);
             if constexpr (PACK_X) keep_packed<VPT>(xv);
-            // x - mean - c is evaluated as (x - mean) - c below.
-            if (valid) {
-#pragma unroll
-                for (int v = 0; v < VPT; ++v) {
+            // x - mean - c is evaluated as (x - mean) - c.
+            if (cur.valid) {
+                static_for<VPT>([&](auto vi) {
+                    constexpr int v = decltype(vi)::value;
                     float o[VEC];
 #pragma unroll
                     for (int i = 0; i < VEC; ++i) {
-                        const float d = (elem<DT, VEC>(xv[v], i) - shift) - c;
+                        const float d = (elem<DT, VEC>(xv[v], i) - mean) - c;
                         const float bias = BIAS ? elem<DT, VEC>(bv[v], i) : 0.0f;
                         o[i] = __builtin_fmaf(d * scale, elem<DT, VEC>(wv[v], i), bias);
                     }
-                    if (in_row(v)) store_raw<DT, VEC, NT_ST>(yp, off.y + col_of(v), make_raw<DT, VEC>(o));
-                }
-            }
-            continue;
-        }
-        if (valid) {
-#pragma unroll
-            for (int v = 0; v < VPT; ++v) {
-                R wr = wv[v];
-                if constexpr (DUAL) wr = second ? wv2[v] : wv[v];
-                float o[VEC];
-#pragma unroll
-                for (int i = 0; i < VEC; ++i)
-                    o[i] = (elem<DT, VEC>(xv[v], i) * scale) * elem<DT, VEC>(wr, i);
-                if (in_row(v)) store_raw<DT, VEC, NT_ST>(yp, off.y + col_of(v), make_raw<DT, VEC>(o));
+                    if (in_row(v))
+                        store_raw<DT, VEC, NT_ST>(cur.yp, cur.off.y + col_of(v),
+                                                  make_raw<DT, VEC>(o));
+                });
             }
         }
     }
@@ -581,10 +605,11 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
         }
 
         if (valid) {
-#pragma unroll
-            for (int v = 0; v < VPT; ++v)
+            static_for<VPT>([&](auto vi) {
+                constexpr int v = decltype(vi)::value;
                 if (in_row(v))
                     store_raw<DT, VEC, NT_ST>(yp, yo + col_of(v), make_raw<DT, VEC>(out[v]));
+            });
         }
         // every lane has read the table before the next block-row rewrites it
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
