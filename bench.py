@@ -158,23 +158,29 @@ def main():
 
     # practical ceiling: the 16-byte copy kernel moving the same bytes as the
     # LayerNorm (the dominant kernel) and as the dual launch (small enough
-    # that the launch's ramp-up and tail show)
+    # that the launch's ramp-up and tail show).  Consecutive copies use
+    # different slices of the 512 MiB LayerNorm buffers, so that, like the
+    # step's kernels, each one reads cold data (a slice read again while
+    # still in the 256 MB MALL would time the cache, not HBM).
     def copy_ceiling(nbytes_each_way):
-        src = dln["x"].view(-1).view(torch.uint8)[:nbytes_each_way]
-        dst = y_ln.view(-1).view(torch.uint8)[:nbytes_each_way]
-        for _ in range(3):
-            trn.bench_copy(src, dst)
+        src_all = dln["x"].view(-1).view(torch.uint8)
+        dst_all = y_ln.view(-1).view(torch.uint8)
+        slices = max(1, src_all.numel() // nbytes_each_way)
+        pairs = [(src_all[i * nbytes_each_way:(i + 1) * nbytes_each_way],
+                  dst_all[i * nbytes_each_way:(i + 1) * nbytes_each_way]) for i in range(slices)]
+        reps = 20
+        for i in range(3):
+            trn.bench_copy(*pairs[i % slices])
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 20
         e0.record(stream)
-        for _ in range(reps):
-            trn.bench_copy(src, dst)
+        for i in range(reps):
+            trn.bench_copy(*pairs[(i + 3) % slices])
         e1.record(stream)
         torch.cuda.synchronize()
         cms = e0.elapsed_time(e1) / reps
         return {"kernel": "copy16 (fnorm_bench_copy)", "bytes": 2 * nbytes_each_way,
-                "avg_ms": round(cms, 5),
+                "avg_ms": round(cms, 5), "distinct_slices": slices,
                 "gbs": round(2 * nbytes_each_way / (cms * 1e-3) / 1e9, 1)}
 
     ceiling = None

@@ -106,6 +106,7 @@ inline void register_dtype(std::vector<Variant>& t) {
     FNORM_EXACT(1, 16, 256, NT_BOTH, 0)
     FNORM_EXACT(1, 16, 256, NT_LOAD, 0)
     FNORM_EXACT(1, 16, 256, NT_NONE, 0)
+    FNORM_EXACT(2, 8, 256, NT_BOTH, 0)
     // 32 packs
     FNORM_EXACT(1, 32, 256, NT_LOAD, 0)
     FNORM_EXACT(2, 16, 256, NT_NONE, 0)
