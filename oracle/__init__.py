@@ -73,6 +73,9 @@ class Oracle:
                                                   ctypes.c_float, ctypes.c_float, _I64, _P, _P,
                                                   _P]
         lib.oracle_dual_head_rms_rope.restype = None
+        lib.oracle_rms_swiglu.argtypes = [_P, _P, _P, ctypes.c_int, _I64, _I64, ctypes.c_float,
+                                          _P]
+        lib.oracle_rms_swiglu.restype = None
         self._lib = lib
 
     @staticmethod
@@ -103,6 +106,23 @@ class Oracle:
         y = np.empty(x.shape, dtype=np.float64)
         self._lib.oracle_rms(self._ptr(x), self._ptr(w), code, rows, width,
                              ctypes.c_float(eps), self._ptr(y))
+        return y
+
+    def rms_swiglu(self, x: np.ndarray, g: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+        """RMSNorm over the last axis times SiLU(g), g of x's shape; float64."""
+        x = np.ascontiguousarray(x)
+        g = np.ascontiguousarray(g)
+        w = np.ascontiguousarray(w)
+        code = self._dtype_code(x)
+        if w.dtype != x.dtype or g.dtype != x.dtype:
+            raise TypeError("x, g and w must share a dtype")
+        width = x.shape[-1]
+        rows = x.size // width if width else 0
+        if w.shape != (width,) or g.shape != x.shape:
+            raise ValueError("w must have shape (width,) and g the shape of x")
+        y = np.empty(x.shape, dtype=np.float64)
+        self._lib.oracle_rms_swiglu(self._ptr(x), self._ptr(g), self._ptr(w), code, rows, width,
+                                    ctypes.c_float(eps), self._ptr(y))
         return y
 
     def layer(self, x: np.ndarray, w: np.ndarray, b: np.ndarray | None, eps: float) -> np.ndarray:

@@ -12,6 +12,9 @@ root).
 Definitions followed:
   - RMSNorm (Emily.Fast docs, `rms_norm`; Emily notebook, Part 1 composed
     cell): y_j = x_j / sqrt(mean_j(x_j^2) + eps) * w_j.
+  - RMSNorm with the SiLU gate (mlx-c-rust `compile/norm_fusion.rs`, the
+    output norm's SwiGLU epilogue, read as y_j = RMSNorm(x, w)_j * g_j /
+    (1 + exp(-g_j))): the exponential taken with `decimal` at 60 digits.
   - LayerNorm (Emily.Fast docs, `layer_norm`): mean and (population) variance
     of the row, y_j = (x_j - mean) / sqrt(var + eps) * w_j + b_j.
 
@@ -67,6 +70,26 @@ def layer_row(x: Sequence[float], w: Sequence[float], b: Sequence[float] | None,
         for xv, wv, bv in zip(xs, w, bias):
             val = _to_decimal((xv - mean) * Fraction(wv)) * s + _to_decimal(bv)
             out.append(float(val))
+        return out
+
+
+def rms_swiglu_row(x: Sequence[float], g: Sequence[float], w: Sequence[float],
+                   eps: float) -> list[float]:
+    """RMSNorm of the row times SiLU of the gate, each value the true result
+    rounded once to a double (up to the 60-digit working precision)."""
+    n = len(x)
+    xs = [Fraction(v) for v in x]
+    denom_sq = sum(v * v for v in xs) / n + Fraction(eps)
+    with localcontext() as ctx:
+        ctx.prec = _DIGITS
+        if denom_sq == 0:
+            return [float("nan")] * n
+        s = _inv_sqrt(denom_sq)
+        out = []
+        for xv, gv, wv in zip(xs, g, w):
+            gd = Decimal(gv)                      # exact: a double is a finite decimal
+            silu = gd / (Decimal(1) + (-gd).exp())
+            out.append(float(_to_decimal(xv * Fraction(wv)) * s * silu))
         return out
 
 

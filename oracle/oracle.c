@@ -43,6 +43,16 @@
  *    through (the docs' "trailing dims" read as the rotated feature count
  *    of the last axis).
  *
+ * RMSNorm with a SwiGLU-style gate epilogue (mlx-c-rust
+ * `compile/norm_fusion.rs`, module docs: the output RMS normalization of the
+ * gated-delta block chained into its "precise SwiGLU" epilogue).  The page
+ * names the chain but does not define SwiGLU; the reading taken:
+ *  - y_j = RMSNorm(x, w)_j * SiLU(g_j), SiLU(g) = g * sigmoid(g)
+ *    = g / (1 + exp(-g)) (the Swish-1 gate of the GLU variants), applied to
+ *    a gate tensor g of x's shape; the normalization itself is unchanged;
+ *  - "precise": no rounding between the norm and the gate; one rounding of
+ *    the final value (in the tests).
+ *
  * Element types: 0 = IEEE binary32, 1 = bfloat16 (the upper 16 bits of a
  * binary32), 2 = IEEE binary16.  All widen to double without rounding.
  *
@@ -214,4 +224,20 @@ void oracle_dual_head_rms_rope(const void *q, const void *k, const void *qw,
                      scale, offset, freqs);
     oracle_rope_rows(ky, tokens * k_heads, k_heads, head_dim, dims, traditional, base,
                      scale, offset, freqs);
+}
+
+/*
+ * RMSNorm followed by the SiLU-gate epilogue, each row:
+ *   y_j = x_j / sqrt(ms + eps) * w_j * g_j / (1 + exp(-g_j))
+ * x, g: rows*width elements; w: width elements; y: rows*width doubles.
+ */
+void oracle_rms_swiglu(const void *x, const void *g, const void *w, int dtype,
+                       int64_t rows, int64_t width, float eps, double *y)
+{
+    oracle_rms(x, w, dtype, rows, width, eps, y);
+    for (int64_t i = 0; i < rows * width; ++i) {
+        double gate = widen(g, dtype, i);
+        double silu = gate / (1.0 + exp(-gate));
+        y[i] = y[i] * silu;
+    }
 }

@@ -367,8 +367,61 @@ def pin_dual_rope(o):
             _close(fk2.reshape(3, 16), rk, 1e-14, floor=1e-12, what="dual rope keys")
 
 
+def _gate_like(rng, dtype, shape):
+    """Gate values over the range where SiLU is neither 0 nor linear, plus
+    a few saturated ones, in the element type of the test."""
+    g = (rng.standard_normal(shape) * 4).astype(np.float32)
+    g.flat[::7] = np.float32(rng.choice([-60.0, -25.0, 25.0, 60.0]))
+    if dtype == "bf16":
+        gb = _bf16_from_f32(g)
+        return gb, _bf16_values(gb)
+    if dtype == "f16":
+        gh = g.astype(np.float16)
+        return gh, gh.astype(np.float64)
+    return g, g.astype(np.float64)
+
+
+def pin_rms_swiglu_bruteforce(o):
+    # exact-rational norm times a 60-digit SiLU, widths 1..16, all types
+    rng = np.random.default_rng(1201)
+    for width in range(1, 17):
+        for dtype in ("f32", "bf16", "f16"):
+            (x, w, _), (xv, wv, _) = _tiny_rows(rng, dtype, width, 2)
+            g, gv = _gate_like(rng, dtype, x.shape)
+            eps = f32(rng.choice([1e-6, 1e-5, 0.5]))
+            got = o.rms_swiglu(x, g, w, eps)
+            exp = np.array([exact_tiny.rms_swiglu_row(xr.tolist(), gr.tolist(), wv.tolist(), eps)
+                            for xr, gr in zip(xv, gv)])
+            _close(got, exp, 1e-13, floor=1e-300, what=f"rms_swiglu width {width} {dtype}")
+
+
+def pin_rms_swiglu_gate_identities(o):
+    rng = np.random.default_rng(1202)
+    x = rng.standard_normal((5, 24)).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, 24).astype(np.float32)
+    plain = o.rms(x, w, f32(1e-6))
+    # SiLU(0) = 0: a zero gate closes the output exactly
+    assert np.all(o.rms_swiglu(x, np.zeros_like(x), w, f32(1e-6)) == 0.0), "zero gate"
+    # SiLU(g) - SiLU(-g) = g (since sigmoid(g) + sigmoid(-g) = 1)
+    g = (rng.standard_normal(x.shape) * 3).astype(np.float32)
+    diff = o.rms_swiglu(x, g, w, f32(1e-6)) - o.rms_swiglu(x, -g, w, f32(1e-6))
+    _close(diff, plain * g.astype(np.float64), 1e-13, floor=1e-12, what="odd part of the gate")
+    # the tanh form of the same gate: SiLU(g) = g/2 * (1 + tanh(g/2))
+    gd = g.astype(np.float64)
+    _close(o.rms_swiglu(x, g, w, f32(1e-6)), plain * gd / 2 * (1 + np.tanh(gd / 2)), 1e-13,
+           floor=1e-12, what="tanh form")
+    # a large gate passes through: SiLU(g) = g (1 - e^-g + ...) -> g
+    big = np.full_like(x, 40.0)
+    _close(o.rms_swiglu(x, big, w, f32(1e-6)), plain * 40.0, 1e-15, what="saturated gate")
+    # the gate does not touch the reduction: rows keep the norm's scale
+    one = np.ones_like(x)
+    _close(o.rms_swiglu(x, one, w, f32(1e-6)), plain / (1 + np.exp(-1.0)), 1e-14,
+           what="unit gate")
+
+
 PINS = [pin_golden_hand_cases, pin_exact_bruteforce_rms, pin_exact_bruteforce_layer,
         pin_rms_unit_invariant, pin_layer_moments, pin_library_identities,
         pin_special_cases, pin_invariances, pin_affine_structure, pin_row_independence,
         pin_bf16_decoding, pin_f16_decoding, pin_dual, pin_rope_norm_and_identity, pin_rope_relative_position,
-        pin_rope_composition_and_scale, pin_rope_layouts_and_table, pin_dual_rope]
+        pin_rope_composition_and_scale, pin_rope_layouts_and_table, pin_dual_rope,
+        pin_rms_swiglu_bruteforce, pin_rms_swiglu_gate_identities]

@@ -80,6 +80,14 @@ MUTANTS = {
     "dual_rope_keys_use_query_heads": (
         "oracle_rope_rows(ky, tokens * k_heads, k_heads,",
         "oracle_rope_rows(ky, tokens * k_heads, q_heads,"),
+    "swiglu_gate_sign": ("double silu = gate / (1.0 + exp(-gate));",
+                         "double silu = gate / (1.0 + exp(gate));"),
+    "swiglu_sigmoid_only": ("double silu = gate / (1.0 + exp(-gate));",
+                            "double silu = 1.0 / (1.0 + exp(-gate));"),
+    "swiglu_gate_reads_x": ("double gate = widen(g, dtype, i);",
+                            "double gate = widen(x, dtype, i);"),
+    "swiglu_gate_dropped": ("y[i] = y[i] * silu;", "y[i] = y[i] * 1.0;"),
+    "swiglu_gate_added": ("y[i] = y[i] * silu;", "y[i] = y[i] + silu;"),
 }
 
 
