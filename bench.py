@@ -19,8 +19,8 @@ than the 256 MB MALL.
 Prints ONE JSON line.  Extra legs (outside the timed region): the plain
 copy kernel over the LayerNorm's bytes (practical ceiling), fused against
 composed (ABBA), the dual launch with RoPE fused in, decode-sized calls
-(eager and HIP-graph replay), and the fp64 CPU oracle over full steps for
-about 10 s (``cpu_baseline``).
+(eager and HIP-graph replay), RMSNorm with the SiLU-gate epilogue, and the
+fp64 CPU oracle over full steps for about 10 s (``cpu_baseline``).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -207,10 +207,12 @@ def main():
     composed = None
     rope = None
     decode = None
+    gated = None
     if not args.no_composed and len(plan) == 3:
         composed = fused_vs_composed(trn, inputs, dev, stream, d, wl_rms, wl_ln, log)
         rope = dual_rope_leg(trn, dq, qy, ky, wl_dual.eps, stream, log)
         decode = decode_leg(trn, dev, stream, log)
+        gated = gated_leg(trn, inputs, dev, stream, log)
 
     cpu = None
     if not args.no_cpu_baseline and len(plan) == 3:
@@ -229,7 +231,7 @@ def main():
                       "parallelism": "rows across workgroups (1 GPU)"},
            "per_op": per_op, "copy_ceiling": ceiling,
            "roofline": roofline, "cpu_baseline": cpu, "fused_vs_composed": composed,
-           "dual_rope": rope, "decode": decode,
+           "dual_rope": rope, "decode": decode, "rms_swiglu": gated,
            "wall_s_timed_region": round(wall, 4)}
     print(json.dumps(out), flush=True)
 
@@ -310,6 +312,47 @@ def dual_rope_leg(trn, dq, qy, ky, eps, stream, log):
                "gbs_min": round(nbytes / (min(v) * 1e-6) / 1e9, 1)} for k, v in times.items()}
     out["kernel"] = trn.describe_rope(trn.BF16, 128, 128, False)
     log(f"[bench] dual + rope: {out}")
+    return out
+
+
+def gated_leg(trn, inputs, dev, stream, log):
+    """RMSNorm with the SiLU-gate epilogue at the gated-delta output-norm
+    shape (4096 tokens x 32 heads x 128, bf16) against the plain RMSNorm of
+    the same x: timed alone and cold (a 512 MiB fill before each call, so
+    that neither arm reads from the MALL), ABBA over 30 reps.  The fused
+    epilogue adds the gate read (6 bytes per element against 4); run as a
+    separate pass it would re-read y and the gate and write y again."""
+    import torch
+
+    wl = inputs.rms_swiglu_bf16_4096tok()
+    x, g, w = (wl.tensors[k].to(dev) for k in ("x", "g", "w"))
+    y = torch.empty_like(x)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    arms = {"rms": lambda: trn.rms_norm(x, w, wl.eps, out=y),
+            "rms_swiglu": lambda: trn.rms_norm_swiglu(x, g, w, wl.eps, out=y)}
+    nbytes = {"rms": 2 * x.numel() * 2, "rms_swiglu": 3 * x.numel() * 2}
+    for f in arms.values():
+        f()
+    torch.cuda.synchronize()
+    times = {k: [] for k in arms}
+    for r in range(30):
+        for k in (list(arms) if r % 2 == 0 else list(arms)[::-1]):
+            flush.fill_(r & 255)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            arms[k]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[k].append(e0.elapsed_time(e1) * 1e3)
+    out = {}
+    for k, v in times.items():
+        v = sorted(v)
+        out[k] = {"min_us": round(v[0], 2), "median_us": round(v[len(v) // 2], 2),
+                  "bytes": nbytes[k], "gbs_median": round(nbytes[k] / (v[len(v) // 2] * 1e-6) / 1e9, 1)}
+    out["shape"] = "x, g [4096, 32, 128] bf16 (131072 rows of 128)"
+    out["kernel"] = trn.describe(trn.OP_RMS_SWIGLU, trn.BF16, 128)
+    del flush
+    log(f"[bench] gated output norm: {out}")
     return out
 
 

@@ -57,7 +57,12 @@ typedef enum {
     FNORM_ERR_WORKSPACE = 8    /* workspace NULL, misaligned, too small or overlapping */
 } fnorm_status;
 
-typedef enum { FNORM_OP_RMS = 0, FNORM_OP_LAYER = 1, FNORM_OP_DUAL = 2 } fnorm_op;
+typedef enum {
+    FNORM_OP_RMS = 0,
+    FNORM_OP_LAYER = 1,
+    FNORM_OP_DUAL = 2,
+    FNORM_OP_RMS_SWIGLU = 3
+} fnorm_op;
 
 /*
  * RMSNorm (Emily.Fast docs, section `rms_norm`; the composed form is the
@@ -77,6 +82,31 @@ int fnorm_rms(const void* x, const void* w, void* y, int64_t rows, int64_t width
  */
 int fnorm_layer(const void* x, const void* w, const void* b, void* y, int64_t rows,
                 int64_t width, float eps, int dtype, void* stream);
+
+/*
+ * RMSNorm with a SiLU-gate epilogue, one pass (the output RMS normalization
+ * of the gated-delta block chained into its SwiGLU epilogue, named in the
+ * mlx-c-rust `compile/norm_fusion.rs` module docs, which rejected the fusion
+ * for want of a pinned summation order):
+ *     y[r, j] = RMSNorm(x, w, eps)[r, j] * SiLU(g[r, j]),
+ *     SiLU(v) = v / (1 + exp(-v))
+ * g (the gate) has x's shape and type.  The page does not define SwiGLU;
+ * this is the gated form of the GLU variants (the gate through SiLU,
+ * multiplying the normalized value), computed in fp32 and rounded once.
+ * The row reduction is the one fnorm_rms uses (same kernel shapes, same
+ * fixed tree), so the epilogue cannot change the summation order.
+ * y may be x or g (in place); other overlaps are FNORM_ERR_ALIAS.  Gates
+ * below about -87 give SiLU values under fp32's normal range.
+ * The _strided form takes row strides (elements) for x, g and y as
+ * fnorm_rms_strided does.
+ */
+int fnorm_rms_swiglu(const void* x, const void* g, const void* w, void* y, int64_t rows,
+                     int64_t width, float eps, int dtype, void* stream);
+int fnorm_rms_swiglu_v(const void* x, const void* g, const void* w, void* y, int64_t rows,
+                       int64_t width, float eps, int dtype, void* stream, int variant);
+int fnorm_rms_swiglu_strided(const void* x, int64_t x_stride, const void* g, int64_t g_stride,
+                             const void* w, void* y, int64_t y_stride, int64_t rows,
+                             int64_t width, float eps, int dtype, void* stream, int variant);
 
 /*
  * Dual-output query/key head RMSNorm in ONE launch (mlx-c-rust

@@ -246,3 +246,24 @@ def test_packed_qkv_layout_is_accepted(lib):
     assert rope(q, k, k, k) == 5
     assert rope(q, k, q, k, kys=kh * hd - 8) == 2
     assert lib.fnorm_last_error().startswith(b"fnorm_dual_head_rms_rope_strided: ")
+
+
+def test_rms_swiglu_validation(lib):
+    G = 0x60000000
+    # (x, g, w, y, rows, width, eps, dtype, stream, variant)
+    sw = lambda *a: lib.fnorm_rms_swiglu_v(*a, None, 10 ** 6)
+    assert sw(A, None, B, C, 4, 8, 1e-6, BF16) == 1          # gate missing
+    assert sw(A, G, B, C, -1, 8, 1e-6, BF16) == 2
+    assert sw(A, G, B, C, 4, 8, -1.0, BF16) == 3
+    assert sw(A, G, B, C, 4, 8, 1e-6, 7) == 4
+    assert sw(A, G, B, G + 16, 4, 8, 1e-6, BF16) == 5         # y partly over the gate
+    assert sw(A, G, B, G, 4, 8, 1e-6, BF16) == 6              # in place on the gate: accepted
+    assert sw(A, G, B, A, 4, 8, 1e-6, BF16) == 6              # in place on x: accepted
+    assert sw(None, None, None, None, 0, 8, 1e-6, BF16) == 0  # no rows: no-op
+    st = lambda *a: lib.fnorm_rms_swiglu_strided(*a, BF16, None, 10 ** 6)
+    # (x, xs, g, gs, w, y, ys, rows, width, eps)
+    assert st(A, 8, G, 7, B, C, 8, 4, 8, 1e-6) == 2           # gate stride below width
+    assert st(A, 16, A + 16, 16, B, C, 8, 4, 8, 1e-6) == 6    # x and g interleaved in one buffer
+    assert lib.fnorm_last_error().startswith(b"fnorm_rms_swiglu_strided: ")
+    assert trn.variant_count(trn.OP_RMS_SWIGLU, BF16, 128) >= 2
+    assert trn.describe(trn.OP_RMS_SWIGLU, BF16, 128).startswith("rmsgate.bf16.vec8.vpt1.lpr16")

@@ -40,3 +40,11 @@ def test_outlier_mask_rate():
     hits = wl.tensors["outliers"]
     assert abs(hits - 0.001 * n) < 5 * np.sqrt(0.001 * n)
     assert abs(float(x[x.abs() < 50].mean()) - 3.0) < 0.05
+
+
+def test_swiglu_workload_shapes():
+    wl = inputs.rms_swiglu_bf16_4096tok(tokens=8)
+    assert wl.tensors["x"].shape == (8, 32, 128) == wl.tensors["g"].shape
+    assert wl.tensors["w"].shape == (128,) and wl.rows == 256 and wl.width == 128
+    again = inputs.rms_swiglu_bf16_4096tok(tokens=8)
+    assert torch.equal(wl.tensors["g"], again.tensors["g"])

@@ -12,6 +12,7 @@ missing, every call raises.
   layer_norm(x, w, b, eps)               LayerNorm over the last axis (b optional)
   dual_head_rms_norm(q, k, qw, kw, eps)  q/k head RMSNorm in one launch
   dual_head_rms_rope(q, k, qw, kw, eps)  the same, with RoPE fused in
+  rms_norm_swiglu(x, g, w, eps)          RMSNorm times SiLU(g), one pass
 Row ops also take row-strided views (e.g. parts of a packed QKV buffer).
 """
 from __future__ import annotations
@@ -25,7 +26,7 @@ LIB_PATH = os.path.join(HERE, "libfnorm.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "fnorm.h")
 
 F32, BF16, F16 = 0, 1, 2
-OP_RMS, OP_LAYER, OP_DUAL = 0, 1, 2
+OP_RMS, OP_LAYER, OP_DUAL, OP_RMS_SWIGLU = 0, 1, 2, 3
 STATUS = {0: "FNORM_OK", 1: "FNORM_ERR_NULL", 2: "FNORM_ERR_SHAPE", 3: "FNORM_ERR_EPS",
           4: "FNORM_ERR_DTYPE", 5: "FNORM_ERR_ALIAS", 6: "FNORM_ERR_UNSUPPORTED",
           7: "FNORM_ERR_LAUNCH", 8: "FNORM_ERR_WORKSPACE"}
@@ -70,6 +71,10 @@ _SIGNATURES = {
     "fnorm_dual_head_rms_rope_strided": ([_P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _I64, _I64,
                                           _I64, _I64, _I64, _F, _I64, _I, _F, _F, _I64, _P, _I,
                                           _P, _I], _I),
+    "fnorm_rms_swiglu": ([_P, _P, _P, _P, _I64, _I64, _F, _I, _P], _I),
+    "fnorm_rms_swiglu_v": ([_P, _P, _P, _P, _I64, _I64, _F, _I, _P, _I], _I),
+    "fnorm_rms_swiglu_strided": ([_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I64, _F, _I, _P, _I],
+                                 _I),
     "fnorm_rms_composed": ([_P, _P, _P, _I64, _I64, _F, _I, _P, _I64, _P], _I),
     "fnorm_layer_composed": ([_P, _P, _P, _P, _I64, _I64, _F, _I, _P, _I64, _P], _I),
 }
@@ -207,6 +212,29 @@ def rms_norm(x, w, eps: float = 1e-6, out=None, variant: int = -1):
     else:
         _check(lib().fnorm_rms_strided(_ptr(x), xs, _ptr(w), _ptr(y), ys, rows, width, eps, code,
                                        _stream(x), variant))
+    return y
+
+
+def rms_norm_swiglu(x, g, w, eps: float = 1e-6, out=None, variant: int = -1):
+    """y = RMSNorm(x, w) * SiLU(g), SiLU(v) = v / (1 + exp(-v)), one pass; g
+    has x's shape and dtype.  x, g and out may be row-strided views."""
+    code = _dtype_code(x)
+    y, rows, width, xs, ys = _rows_io(x, out)
+    _check_dev(g, "g", x.dtype, x.device)
+    if g.shape != x.shape:
+        raise ValueError("g must have x's shape")
+    _require(w, "w", x.dtype, x.device)
+    if tuple(w.shape) != (width,):
+        raise ValueError(f"w has shape {tuple(w.shape)}, expected ({width},)")
+    if xs is None and g.is_contiguous():
+        _check(lib().fnorm_rms_swiglu_v(_ptr(x), _ptr(g), _ptr(w), _ptr(y), rows, width, eps,
+                                        code, _stream(x), variant))
+    else:
+        xs = _row_stride(x, "x") if xs is None else xs
+        ys = _row_stride(y, "out") if ys is None else ys
+        _check(lib().fnorm_rms_swiglu_strided(_ptr(x), xs, _ptr(g), _row_stride(g, "g"), _ptr(w),
+                                              _ptr(y), ys, rows, width, eps, code, _stream(x),
+                                              variant))
     return y
 
 

@@ -110,7 +110,7 @@ int candidates(int kind, int dt, int64_t width, bool aligned, const Variant** ou
         if (const Variant* m = smallest_masked(kind, dt, vec, width)) out[n++] = m;
     }
     if (const Variant* s = smallest_masked(kind, dt, 1, width)) out[n++] = s;
-    if (kind == K_RMS || kind == K_LAYER || kind == K_LAYER_NOBIAS) {
+    if (kind == K_RMS || kind == K_LAYER || kind == K_LAYER_NOBIAS || kind == K_RMS_GATED) {
         if (vec_ok)
             if (const Variant* w = find_wide(kind, dt, vec)) out[n++] = w;
         if (const Variant* w = find_wide(kind, dt, 1)) out[n++] = w;
@@ -181,6 +181,7 @@ bool pick(int kind, int dt, int64_t width, bool aligned, int variant, Choice* c)
 int op_kind(int op, bool has_bias) {
     if (op == FNORM_OP_RMS) return K_RMS;
     if (op == FNORM_OP_LAYER) return has_bias ? K_LAYER : K_LAYER_NOBIAS;
+    if (op == FNORM_OP_RMS_SWIGLU) return K_RMS_GATED;
     return K_DUAL;
 }
 
@@ -188,7 +189,8 @@ void describe_choice(const Choice& c, char* buf, size_t len) {
     const Variant& v = *c.v;
     static const char* nts[] = {"", ".ntst", ".ntld", ".nt"};
     const char* nt = nts[(v.nt & NT_LOAD ? 2 : 0) | (v.nt & NT_STORE ? 1 : 0)];
-    static const char* kinds[] = {"rms", "layer", "layer", "dual", "copy", "ropesplit", "ropeinter"};
+    static const char* kinds[] = {"rms",       "layer",     "layer",  "dual",
+                                  "copy",      "ropesplit", "ropeinter", "rmsgate"};
     if (v.wide)
         std::snprintf(buf, len, "%s.%s.vec%d.wide.blk%d.%s", kinds[v.kind], dtype_name(v.dt),
                       v.vec, v.block, c.persistent ? "persistent" : "grid");
@@ -333,33 +335,42 @@ bool output_clashes(const Span& y, const Span& x) {
 bool stride_aligned(int64_t stride_elems, int64_t eb) { return (stride_elems * eb) % 16 == 0; }
 
 // RMSNorm / LayerNorm over rows addressed with row strides (elements).
-int rows_impl(const char* op, bool layer, const void* x, int64_t xs, const void* w,
-              const void* b, void* y, int64_t ys, int64_t rows, int64_t width, float eps,
-              int dtype, void* stream, int variant) {
+int rows_impl(const char* op, int fop, const void* x, int64_t xs, const void* g, int64_t gs,
+              const void* w, const void* b, void* y, int64_t ys, int64_t rows, int64_t width,
+              float eps, int dtype, void* stream, int variant) {
+    const bool gated = fop == FNORM_OP_RMS_SWIGLU;
     if (int s = check_scalars(op, dtype, rows, width, eps)) return s;
-    if (rows > 1 && (xs < width || ys < width))
-        return fail(FNORM_ERR_SHAPE, op, "row strides (%lld, %lld) below width %lld",
-                    (long long)xs, (long long)ys, (long long)width);
-    if (rows > 1 && (xs > (INT64_MAX / 8) / rows || ys > (INT64_MAX / 8) / rows))
+    if (rows > 1 && (xs < width || ys < width || (gated && gs < width)))
+        return fail(FNORM_ERR_SHAPE, op, "row strides below width %lld", (long long)width);
+    if (rows > 1 && (xs > (INT64_MAX / 8) / rows || ys > (INT64_MAX / 8) / rows ||
+                     (gated && gs > (INT64_MAX / 8) / rows)))
         return fail(FNORM_ERR_SHAPE, op, "row strides overflow");
     if (rows == 0) return ok();
     if (!x || !w || !y) return fail(FNORM_ERR_NULL, op, "x, w and y must be non-NULL");
+    if (gated && !g) return fail(FNORM_ERR_NULL, op, "the gate must be non-NULL");
     const int64_t eb = elem_bytes(dtype);
     const Span sx = span(x, xs, width, rows, eb), sy = span(y, ys, width, rows, eb);
     const Span sw = span(w, width, width, 1, eb), sb = span(b, width, width, 1, eb);
+    const Span sg = span(g, gs, width, gated ? rows : 0, eb);
     if (output_clashes(sy, sx))
         return fail(FNORM_ERR_ALIAS, op, "y overlaps x without being x itself");
+    if (output_clashes(sy, sg))
+        return fail(FNORM_ERR_ALIAS, op, "y overlaps the gate without being the gate itself");
     if (spans_overlap(sy, sw)) return fail(FNORM_ERR_ALIAS, op, "y overlaps w");
     if (spans_overlap(sy, sb)) return fail(FNORM_ERR_ALIAS, op, "y overlaps b");
+    const bool one = rows == 1;
     const bool al = aligned16(x) && aligned16(w) && aligned16(y) && (!b || aligned16(b)) &&
-                    (rows == 1 || (stride_aligned(xs, eb) && stride_aligned(ys, eb)));
+                    (!gated || aligned16(g)) &&
+                    (one || (stride_aligned(xs, eb) && stride_aligned(ys, eb) &&
+                             (!gated || stride_aligned(gs, eb))));
     Choice c;
-    const int kind = layer ? op_kind(FNORM_OP_LAYER, b != nullptr) : K_RMS;
+    const int kind = op_kind(fop, b != nullptr);
     if (!pick(kind, dtype, width, al, variant, &c))
         return fail(FNORM_ERR_UNSUPPORTED, op, "no kernel variant %d for width %lld", variant,
                     (long long)width);
     NormArgs a{x,    w,    b,     y,     nullptr, nullptr, nullptr, rows, rows, width,
-               eps,  rows == 1 ? width : xs, rows == 1 ? width : ys, 1, width, width, 1};
+               eps,  one ? width : xs, one ? width : ys, 1, width, width, 1,
+               gated ? g : nullptr, one ? width : gs};
     return launch(op, c, a, stream);
 }
 
@@ -502,8 +513,8 @@ extern "C" {
 
 int fnorm_rms_v(const void* x, const void* w, void* y, int64_t rows, int64_t width, float eps,
                 int dtype, void* stream, int variant) {
-    return rows_impl("fnorm_rms", false, x, width, w, nullptr, y, width, rows, width, eps, dtype,
-                     stream, variant);
+    return rows_impl("fnorm_rms", FNORM_OP_RMS, x, width, nullptr, 0, w, nullptr, y, width, rows,
+                     width, eps, dtype, stream, variant);
 }
 
 int fnorm_rms(const void* x, const void* w, void* y, int64_t rows, int64_t width, float eps,
@@ -514,14 +525,14 @@ int fnorm_rms(const void* x, const void* w, void* y, int64_t rows, int64_t width
 int fnorm_rms_strided(const void* x, int64_t x_stride, const void* w, void* y, int64_t y_stride,
                       int64_t rows, int64_t width, float eps, int dtype, void* stream,
                       int variant) {
-    return rows_impl("fnorm_rms_strided", false, x, x_stride, w, nullptr, y, y_stride, rows,
-                     width, eps, dtype, stream, variant);
+    return rows_impl("fnorm_rms_strided", FNORM_OP_RMS, x, x_stride, nullptr, 0, w, nullptr, y,
+                     y_stride, rows, width, eps, dtype, stream, variant);
 }
 
 int fnorm_layer_v(const void* x, const void* w, const void* b, void* y, int64_t rows,
                   int64_t width, float eps, int dtype, void* stream, int variant) {
-    return rows_impl("fnorm_layer", true, x, width, w, b, y, width, rows, width, eps, dtype,
-                     stream, variant);
+    return rows_impl("fnorm_layer", FNORM_OP_LAYER, x, width, nullptr, 0, w, b, y, width, rows,
+                     width, eps, dtype, stream, variant);
 }
 
 int fnorm_layer(const void* x, const void* w, const void* b, void* y, int64_t rows,
@@ -532,8 +543,26 @@ int fnorm_layer(const void* x, const void* w, const void* b, void* y, int64_t ro
 int fnorm_layer_strided(const void* x, int64_t x_stride, const void* w, const void* b, void* y,
                         int64_t y_stride, int64_t rows, int64_t width, float eps, int dtype,
                         void* stream, int variant) {
-    return rows_impl("fnorm_layer_strided", true, x, x_stride, w, b, y, y_stride, rows, width,
-                     eps, dtype, stream, variant);
+    return rows_impl("fnorm_layer_strided", FNORM_OP_LAYER, x, x_stride, nullptr, 0, w, b, y,
+                     y_stride, rows, width, eps, dtype, stream, variant);
+}
+
+int fnorm_rms_swiglu_v(const void* x, const void* g, const void* w, void* y, int64_t rows,
+                       int64_t width, float eps, int dtype, void* stream, int variant) {
+    return rows_impl("fnorm_rms_swiglu", FNORM_OP_RMS_SWIGLU, x, width, g, width, w, nullptr, y,
+                     width, rows, width, eps, dtype, stream, variant);
+}
+
+int fnorm_rms_swiglu(const void* x, const void* g, const void* w, void* y, int64_t rows,
+                     int64_t width, float eps, int dtype, void* stream) {
+    return fnorm_rms_swiglu_v(x, g, w, y, rows, width, eps, dtype, stream, -1);
+}
+
+int fnorm_rms_swiglu_strided(const void* x, int64_t x_stride, const void* g, int64_t g_stride,
+                             const void* w, void* y, int64_t y_stride, int64_t rows,
+                             int64_t width, float eps, int dtype, void* stream, int variant) {
+    return rows_impl("fnorm_rms_swiglu_strided", FNORM_OP_RMS_SWIGLU, x, x_stride, g, g_stride,
+                     w, nullptr, y, y_stride, rows, width, eps, dtype, stream, variant);
 }
 
 int fnorm_dual_head_rms_v(const void* q, const void* k, const void* qw, const void* kw, void* qy,
@@ -600,7 +629,7 @@ int fnorm_dual_head_rms_rope_strided(const void* q, int64_t q_stride, const void
 }
 
 int fnorm_variant_count(int op, int dtype, int64_t width, int aligned) {
-    if (!valid_dtype(dtype) || width <= 0 || op < 0 || op > 2) return 0;
+    if (!valid_dtype(dtype) || width <= 0 || op < 0 || op > 3) return 0;
     const Variant* list[kMaxCandidates];
     return 2 * candidates(op_kind(op, true), dtype, width, aligned != 0, list);
 }
@@ -612,7 +641,7 @@ int fnorm_describe(int op, int dtype, int64_t width, int aligned, int variant, c
     buf[0] = '\0';
     if (!valid_dtype(dtype)) return fail(FNORM_ERR_DTYPE, name, "dtype %d", dtype);
     if (width <= 0) return fail(FNORM_ERR_SHAPE, name, "width %lld", (long long)width);
-    if (op < 0 || op > 2) return fail(FNORM_ERR_UNSUPPORTED, name, "op %d", op);
+    if (op < 0 || op > 3) return fail(FNORM_ERR_UNSUPPORTED, name, "op %d", op);
     Choice c;
     if (!pick(op_kind(op, true), dtype, width, aligned != 0, variant, &c))
         return fail(FNORM_ERR_UNSUPPORTED, name, "no variant %d", variant);

@@ -20,7 +20,9 @@
 namespace fnorm {
 
 enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
-enum : int { OP_RMS = 0, OP_LAYER = 1 };
+// OP_RMS_GATED: RMSNorm whose output is multiplied by SiLU(gate), the gate
+// a second tensor of x's shape (the output norm's gate epilogue).
+enum : int { OP_RMS = 0, OP_LAYER = 1, OP_RMS_GATED = 2 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -62,6 +64,15 @@ __device__ __forceinline__ typename Raw<DT, VEC>::type load_raw(const void* base
                                             idx * Elem<DT>::bytes);
     if constexpr (NT) return __builtin_nontemporal_load(p);
     else return *p;
+}
+
+// SiLU(g) = g * sigmoid(g) in fp32, in a form that cannot overflow:
+// e = exp(-|g|) lies in (0, 1], sigmoid(|g|) = 1 / (1 + e), and
+// sigmoid(-|g|) = e / (1 + e).
+__device__ __forceinline__ float silu(float g) {
+    const float e = expf(-__builtin_fabsf(g));
+    const float r = 1.0f / (1.0f + e);
+    return g * (g >= 0.0f ? r : e * r);
 }
 
 // f(0), f(1), ..., f(N-1) with compile-time indices and no loop in the IR.

@@ -12,9 +12,16 @@
 
 namespace fnorm {
 
+template <int KIND>
+constexpr int op_of() {
+    return (KIND == K_LAYER || KIND == K_LAYER_NOBIAS) ? OP_LAYER
+           : KIND == K_RMS_GATED                      ? OP_RMS_GATED
+                                                      : OP_RMS;
+}
+
 template <int KIND, int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, int NT>
 inline Variant make_variant(int cap) {
-    constexpr int OP = (KIND == K_LAYER || KIND == K_LAYER_NOBIAS) ? OP_LAYER : OP_RMS;
+    constexpr int OP = op_of<KIND>();
     constexpr bool BIAS = KIND == K_LAYER;
     constexpr bool DUAL = KIND == K_DUAL;
     Variant v{};
@@ -39,11 +46,12 @@ inline void add_shape(std::vector<Variant>& t, int cap = 0) {
     t.push_back(make_variant<K_LAYER, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
     t.push_back(make_variant<K_LAYER_NOBIAS, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
     t.push_back(make_variant<K_DUAL, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
+    t.push_back(make_variant<K_RMS_GATED, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
 }
 
 template <int KIND, int DT, int VEC, int BLOCK>
 inline Variant make_wide() {
-    constexpr int OP = (KIND == K_LAYER || KIND == K_LAYER_NOBIAS) ? OP_LAYER : OP_RMS;
+    constexpr int OP = op_of<KIND>();
     Variant v{};
     v.fn = reinterpret_cast<const void*>(&norm_rows_wide<OP, DT, VEC, BLOCK, KIND == K_LAYER>);
     v.kind = KIND;
@@ -64,6 +72,7 @@ inline void add_wide(std::vector<Variant>& t) {
     t.push_back(make_wide<K_RMS, DT, VEC, 1024>());
     t.push_back(make_wide<K_LAYER, DT, VEC, 1024>());
     t.push_back(make_wide<K_LAYER_NOBIAS, DT, VEC, 1024>());
+    t.push_back(make_wide<K_RMS_GATED, DT, VEC, 1024>());
 }
 
 // Masked shapes for any width up to 8192 packs, used with pack width V

@@ -57,6 +57,9 @@ struct NormArgs {
     // likewise with x2h, x2s, y2s.
     int64_t xs, ys, xh;
     int64_t x2s, y2s, x2h;
+    // OP_RMS_GATED only: the gate, row r at r * gs (one row per token).
+    const void* g;
+    int64_t gs;
 };
 
 struct RowOff {
@@ -80,8 +83,10 @@ template <int OP, int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, boo
 __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
     constexpr bool NT_LD = (NT & NT_LOAD) != 0;
     constexpr bool NT_ST = (NT & NT_STORE) != 0;
+    constexpr bool GATED = OP == OP_RMS_GATED;
     using R = typename Raw<DT, VEC>::type;
     static_assert(BLOCK % 64 == 0 && BLOCK % LPR == 0, "launch shape");
+    static_assert(!(GATED && (DUAL || BIAS)), "the gate goes with plain RMSNorm");
     constexpr int RPB = BLOCK / LPR;                 // rows per block-row
     constexpr int WPR = LPR > 64 ? LPR / 64 : 1;     // waves per row
     constexpr int LDS_SLOTS = LPR > 64 ? RPB * WPR : 1;
@@ -127,6 +132,7 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
         const void* xp;
         void* yp;
         RowOff off;
+        int64_t goff;
     };
     auto locate = [&](int64_t base) {
         Loc L;
@@ -146,12 +152,19 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
         }
         L.off = L.second ? row_offsets(r, a.x2h, a.x2s, a.y2s, width)
                          : row_offsets(r, a.xh, a.xs, a.ys, width);
+        L.goff = GATED ? r * a.gs : 0;
         return L;
     };
     auto load_row = [&](const Loc& L, R* dst) {
 #pragma unroll
         for (int v = 0; v < VPT; ++v)
             dst[v] = in_row(v) ? load_raw<DT, VEC, NT_LD>(L.xp, L.off.x + col_of(v))
+                               : raw_zero<DT, VEC>();
+    };
+    auto load_gate = [&](const Loc& L, R* dst) {
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+            dst[v] = in_row(v) ? load_raw<DT, VEC, NT_LD>(a.g, L.goff + col_of(v))
                                : raw_zero<DT, VEC>();
     };
 
@@ -161,6 +174,8 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
         const Loc cur = locate(base);
         R xv[VPT];
         load_row(cur, xv);
+        R gv[GATED ? VPT : 1];
+        if constexpr (GATED) load_gate(cur, gv);
         if constexpr (PACK_W) {
             keep_packed<VPT>(wv);
             if constexpr (BIAS) keep_packed<VPT>(bv);
@@ -168,7 +183,7 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
         }
 
         // Row scalars, then out = (x - shift) * scale * w + bias.
-        if constexpr (OP == OP_RMS) {
+        if constexpr (OP == OP_RMS || GATED) {
             float ss = 0.0f;
 #pragma unroll
             for (int v = 0; v < VPT; ++v)
@@ -181,6 +196,7 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
             parity ^= 1;
             const float scale = __builtin_amdgcn_rsqf(ss / fwidth + a.eps);
             if constexpr (PACK_X) keep_packed<VPT>(xv);
+            if constexpr (GATED && PACK_X) keep_packed<VPT>(gv);
             if (cur.valid) {
                 static_for<VPT>([&](auto vi) {
                     constexpr int v = decltype(vi)::value;
@@ -197,6 +213,10 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
 #pragma unroll
                     for (int i = 0; i < VEC; ++i)
                         o[i] = (elem<DT, VEC>(xv[v], i) * scale) * elem<DT, VEC>(wr, i);
+                    if constexpr (GATED) {
+#pragma unroll
+                        for (int i = 0; i < VEC; ++i) o[i] *= silu(elem<DT, VEC>(gv[v], i));
+                    }
                     if (in_row(v))
                         store_raw<DT, VEC, NT_ST>(cur.yp, cur.off.y + col_of(v),
                                                   make_raw<DT, VEC>(o));
@@ -253,7 +273,8 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
 // BLOCK * VEC.  RMSNorm: one pass for sum(x^2), one to normalize.
 // LayerNorm: one pass for the mean, one for the squared deviations, one to
 // normalize (the same corrected two-pass as above).  The dual form is not
-// offered here; rows are addressed with a plain row stride (xh = 1).
+// offered here; rows are addressed with a plain row stride (xh = 1).  The
+// gated RMSNorm reads its gate in the last pass.
 template <int OP, int DT, int VEC, int BLOCK, bool BIAS>
 __global__ __launch_bounds__(BLOCK) void norm_rows_wide(NormArgs a) {
     using R = typename Raw<DT, VEC>::type;
@@ -267,7 +288,7 @@ __global__ __launch_bounds__(BLOCK) void norm_rows_wide(NormArgs a) {
         const int64_t off = row * a.xs;
         const int64_t yoff = row * a.ys;
         float s, mean = 0.0f, c = 0.0f;
-        if constexpr (OP == OP_RMS) {
+        if constexpr (OP == OP_RMS || OP == OP_RMS_GATED) {
             float ss = 0.0f;
             for (int64_t col = int64_t(tid) * VEC; col < width; col += STEP) {
                 const R xr = load_raw<DT, VEC, false>(a.x, off + col);
@@ -307,9 +328,14 @@ __global__ __launch_bounds__(BLOCK) void norm_rows_wide(NormArgs a) {
             const R xr = load_raw<DT, VEC, false>(a.x, off + col);
             const R wr = load_raw<DT, VEC, false>(a.w, col);
             float o[VEC];
-            if constexpr (OP == OP_RMS) {
+            if constexpr (OP == OP_RMS || OP == OP_RMS_GATED) {
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) o[i] = (elem<DT, VEC>(xr, i) * s) * elem<DT, VEC>(wr, i);
+                if constexpr (OP == OP_RMS_GATED) {
+                    const R gr = load_raw<DT, VEC, false>(a.g, row * a.gs + col);
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) o[i] *= silu(elem<DT, VEC>(gr, i));
+                }
             } else {
                 R br = raw_zero<DT, VEC>();
                 if constexpr (BIAS) br = load_raw<DT, VEC, false>(a.b, col);

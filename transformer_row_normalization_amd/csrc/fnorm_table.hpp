@@ -15,7 +15,8 @@ namespace fnorm {
 
 enum Kind : int {
     K_RMS = 0, K_LAYER = 1, K_LAYER_NOBIAS = 2, K_DUAL = 3, K_COPY = 4,
-    K_ROPE_SPLIT = 5, K_ROPE_TRAD = 6   // dual head RMSNorm + RoPE (split-half / interleaved)
+    K_ROPE_SPLIT = 5, K_ROPE_TRAD = 6,  // dual head RMSNorm + RoPE (split-half / interleaved)
+    K_RMS_GATED = 7                     // RMSNorm times SiLU(gate)
 };
 
 struct Variant {

@@ -22,6 +22,10 @@ Workloads (name: shape, distribution):
   layer_bf16_65536x4096 x [65536,4096] ~ N(3,1) with a Bernoulli(0.001) mask
                         of entries multiplied by 100, w ~ N(1,0.1),
                         b ~ N(0,0.02), eps 1e-5.
+  rms_swiglu_bf16_4096tok  the gated output norm of a gated-delta block at
+                        the dual workload's head layout: x [4096,32,128]
+                        ~ N(0,1), gate g [4096,32,128] ~ N(0,2),
+                        w [128] ~ N(1,0.1), eps 1e-6.
 """
 from __future__ import annotations
 
@@ -33,7 +37,7 @@ import torch
 @dataclass
 class Workload:
     name: str
-    op: str                      # "rms" | "layer" | "dual"
+    op: str                      # "rms" | "layer" | "dual" | "swiglu"
     dtype: torch.dtype
     eps: float
     tensors: dict = field(default_factory=dict)
@@ -130,15 +134,28 @@ def layer_bf16_65536x4096(rows: int = 65536, width: int = 4096) -> Workload:
     return wl
 
 
+def rms_swiglu_bf16_4096tok(tokens: int = 4096, heads: int = 32,
+                            head_dim: int = 128) -> Workload:
+    g = _gen(5)
+    x = normal((tokens, heads, head_dim), 0.0, 1.0, g).to(torch.bfloat16)
+    gate = normal((tokens, heads, head_dim), 0.0, 2.0, g).to(torch.bfloat16)
+    w = normal((head_dim,), 1.0, 0.1, g).to(torch.bfloat16)
+    return Workload(f"rms_swiglu_bf16_{tokens}tok", "swiglu", torch.bfloat16, 1e-6,
+                    {"x": x, "g": gate, "w": w})
+
+
 def random_rows(op: str, rows: int, width: int, dtype: torch.dtype, seed: int,
                 mean: float = 0.0, std: float = 1.0, with_bias: bool = True) -> dict:
     """Generic seeded inputs of any shape, for sweeps: x ~ N(mean, std),
-    w ~ N(1, 0.1), b ~ N(0, 0.02)."""
+    w ~ N(1, 0.1), b ~ N(0, 0.02) (LayerNorm), gate g ~ N(0, 3) (op
+    "swiglu")."""
     g = _gen(seed)
     out = {"x": normal((rows, width), mean, std, g).to(dtype),
            "w": normal((width,), 1.0, 0.1, g).to(dtype)}
     if op == "layer" and with_bias:
         out["b"] = normal((width,), 0.0, 0.02, g).to(dtype)
+    if op == "swiglu":
+        out["g"] = normal((rows, width), 0.0, 3.0, g).to(dtype)
     return out
 
 
@@ -148,4 +165,5 @@ ALL = {
     "dual_bf16_4096tok": dual_bf16_4096tok,
     "rms_bf16_16384x8192": rms_bf16_16384x8192,
     "layer_bf16_65536x4096": layer_bf16_65536x4096,
+    "rms_swiglu_bf16_4096tok": rms_swiglu_bf16_4096tok,
 }
