@@ -68,10 +68,23 @@ __device__ __forceinline__ typename Raw<DT, VEC>::type load_raw(const void* base
 
 // SiLU(g) = g * sigmoid(g) in fp32, in a form that cannot overflow:
 // e = exp(-|g|) lies in (0, 1], sigmoid(|g|) = 1 / (1 + e), and
-// sigmoid(-|g|) = e / (1 + e).
+// sigmoid(-|g|) = e / (1 + e).  e comes from the hardware base-2
+// exponential (v_exp_f32) of -|g| log2(e); the product |g| log2(e) is
+// carried as p + lo (lo from an fma remainder and the low part of log2(e)),
+// so its rounding error does not grow with |g|, and exp2(-lo) is applied to
+// first order (|lo| < 2^-17).  With the hardware reciprocal the result is
+// within a few fp32 ulp; gates below about -87 give values under fp32's
+// normal range.  (An expf and an IEEE division here made the gated kernel
+// ALU-bound.)
 __device__ __forceinline__ float silu(float g) {
-    const float e = expf(-__builtin_fabsf(g));
-    const float r = 1.0f / (1.0f + e);
+    constexpr float kLog2e = 1.44269502163f;      // log2(e) rounded to fp32
+    constexpr float kLog2eLo = 1.92596303e-08f;   // log2(e) - kLog2e
+    constexpr float kLn2 = 0.693147182f;
+    const float a = __builtin_fabsf(g);
+    const float p = a * kLog2e;
+    const float lo = __builtin_fmaf(a, kLog2e, -p) + a * kLog2eLo;
+    const float e = __builtin_amdgcn_exp2f(-p) * __builtin_fmaf(-lo, kLn2, 1.0f);
+    const float r = __builtin_amdgcn_rcpf(1.0f + e);
     return g * (g >= 0.0f ? r : e * r);
 }
 
