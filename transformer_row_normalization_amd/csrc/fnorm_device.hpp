@@ -200,26 +200,45 @@ constexpr int DPP_ROW_SHL4 = 0x104;   // lane l <- lane l + 4
 constexpr int DPP_ROW_SHR4 = 0x114;   // lane l <- lane l - 4
 constexpr int DPP_ROW_ROR8 = 0x128;   // lane l <- lane l ^ 8 (rotate by 8 of 16)
 
-// The value held by lane (l ^ d) of the wavefront, for a pair distance d
-// that is a power of two, through the cheapest path: DPP for d <= 8,
-// ds_swizzle for d = 16, ds_bpermute otherwise (also for d not a power of
-// two, where `bperm_addr` names the source lane * 4).
-__device__ __forceinline__ float lane_partner(float v, int d, int wave_lane, int bperm_addr) {
+// Value of `v` held by the lane at distance D within the row group (the
+// split-half RoPE partner), D a compile-time distance: DPP for D = 1, 2, 4,
+// 8 (inside a 16-lane row), ds_swizzle for D = 16, and ds_bpermute from
+// `bperm_addr` (source lane * 4) for D = 0, meaning any other distance.
+template <int D>
+__device__ __forceinline__ float lane_partner(float v, int wave_lane, int bperm_addr) {
+    if constexpr (D == 1) {
+        return dpp<DPP_QUAD_1032>(v);
+    } else if constexpr (D == 2) {
+        return dpp<DPP_QUAD_2301>(v);
+    } else if constexpr (D == 4) {
+        const float up = dpp<DPP_ROW_SHL4>(v);
+        const float down = dpp<DPP_ROW_SHR4>(v);
+        return (wave_lane & 4) ? down : up;
+    } else if constexpr (D == 8) {
+        return dpp<DPP_ROW_ROR8>(v);
+    } else if constexpr (D == 16) {
+        return __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), SWIZZLE_XOR16));
+    } else {
+        static_assert(D == 0, "partner distance");
+        return __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute(bperm_addr, __builtin_bit_cast(int, v)));
+    }
+}
+
+// Calls f(std::integral_constant<int, D>) with D the compile-time form of
+// the runtime partner distance d (0 for distances without a DPP/swizzle
+// pattern), so that the choice is one uniform branch per row, not one per
+// element.
+template <class F>
+__device__ __forceinline__ void with_partner_distance(int d, F&& f) {
     switch (d) {
-        case 1: return dpp<DPP_QUAD_1032>(v);
-        case 2: return dpp<DPP_QUAD_2301>(v);
-        case 4: {
-            const float up = dpp<DPP_ROW_SHL4>(v);
-            const float down = dpp<DPP_ROW_SHR4>(v);
-            return (wave_lane & 4) ? down : up;
-        }
-        case 8: return dpp<DPP_ROW_ROR8>(v);
-        case 16:
-            return __builtin_bit_cast(
-                float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), SWIZZLE_XOR16));
-        default:
-            return __builtin_bit_cast(
-                float, __builtin_amdgcn_ds_bpermute(bperm_addr, __builtin_bit_cast(int, v)));
+        case 1: f(std::integral_constant<int, 1>{}); break;
+        case 2: f(std::integral_constant<int, 2>{}); break;
+        case 4: f(std::integral_constant<int, 4>{}); break;
+        case 8: f(std::integral_constant<int, 8>{}); break;
+        case 16: f(std::integral_constant<int, 16>{}); break;
+        default: f(std::integral_constant<int, 0>{}); break;
     }
 }
 
