@@ -4,6 +4,9 @@ and rejects invalid arguments before any HIP call (no device needed).
 Pointers here are fake addresses: every call below fails validation, which
 runs before the library touches HIP, so nothing is launched."""
 import ctypes
+import os
+import shutil
+import subprocess
 
 import pytest
 
@@ -267,3 +270,19 @@ def test_rms_swiglu_validation(lib):
     assert lib.fnorm_last_error().startswith(b"fnorm_rms_swiglu_strided: ")
     assert trn.variant_count(trn.OP_RMS_SWIGLU, BF16, 128) >= 2
     assert trn.describe(trn.OP_RMS_SWIGLU, BF16, 128).startswith("rmsgate.bf16.vec8.vpt1.lpr16")
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_header_compiles_as_c_and_links(tmp_path):
+    """include/fnorm.h is valid C11; a C program links libfnorm.so and sees
+    the documented status codes (validation only, no GPU needed)."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = tmp_path / "abi_check"
+    libdir = os.path.dirname(trn.LIB_PATH)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I", os.path.join(root, "include"),
+                    os.path.join(root, "tests", "c_abi", "abi_check.c"), "-o", str(exe),
+                    "-L", libdir, "-lfnorm", "-Wl,-rpath," + libdir], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert "c abi ok" in out.stdout

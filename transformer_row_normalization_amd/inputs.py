@@ -159,6 +159,24 @@ def random_rows(op: str, rows: int, width: int, dtype: torch.dtype, seed: int,
     return out
 
 
+def large_rows_on_device(rows: int, width: int, dtype: torch.dtype, seed: int, device,
+                         mean: float = 0.0, std: float = 1.0) -> dict:
+    """Rows too large to build on the host (past 2^31 elements): x ~ N(mean,
+    std) drawn by the device's seeded generator in fp32 slabs, cast once;
+    w ~ N(1, 0.1) and b ~ N(0, 0.02) from the CPU generator.  Returns device
+    tensors; callers copy sampled rows back for the oracle."""
+    gdev = torch.Generator(device=device).manual_seed(seed)
+    x = torch.empty((rows, width), dtype=dtype, device=device)
+    slab = max(1, (1 << 27) // width)
+    for r0 in range(0, rows, slab):
+        n = min(slab, rows - r0)
+        x[r0:r0 + n] = (torch.randn((n, width), generator=gdev, device=device,
+                                    dtype=torch.float32) * std + mean).to(dtype)
+    g = _gen(seed)
+    return {"x": x, "w": normal((width,), 1.0, 0.1, g).to(dtype).to(device),
+            "b": normal((width,), 0.0, 0.02, g).to(dtype).to(device)}
+
+
 ALL = {
     "rms_f32_512x1024": rms_f32_512x1024,
     "layer_f32_1024x768": layer_f32_1024x768,
