@@ -363,7 +363,9 @@ def decode_leg(trn, dev, stream, log):
     launches (q, then k), the one dual launch, and the dual launch with RoPE
     (position 1000 + token).  Timed two ways, ABBA over the arms:
       eager  - 200 back-to-back calls between two events: what a host loop
-               sustains, launch submission included;
+               sustains, launch submission included ("dual_c_abi" calls the
+               C entry point directly with prepared arguments, leaving out
+               the Python binding's checks);
       graph  - one HIP graph holding 64 calls, replayed 10 times: device
                time per call with the host out of the loop."""
     import torch
@@ -377,7 +379,15 @@ def decode_leg(trn, dev, stream, log):
         qw = (1 + 0.1 * torch.randn(hd, generator=g)).to(torch.bfloat16).to(dev)
         kw = (1 + 0.1 * torch.randn(hd, generator=g)).to(torch.bfloat16).to(dev)
         qy, ky = torch.empty_like(q), torch.empty_like(k)
+        # the C entry point called directly with prepared arguments: the
+        # library's own host cost per launch, without the binding's checks
+        import ctypes
+        c_args = tuple(ctypes.c_void_p(t.data_ptr()) for t in (q, k, qw, kw, qy, ky)) + (
+            tokens * qh, tokens * kh, hd, ctypes.c_float(1e-6), trn.BF16,
+            ctypes.c_void_p(stream.cuda_stream))
+        c_dual = trn.lib().fnorm_dual_head_rms
         arms = {
+            "dual_c_abi": lambda: c_dual(*c_args),
             "two_rms": lambda: (trn.rms_norm(q, qw, 1e-6, out=qy), trn.rms_norm(k, kw, 1e-6, out=ky)),
             "dual": lambda: trn.dual_head_rms_norm(q, k, qw, kw, 1e-6, q_out=qy, k_out=ky),
             "dual_rope": lambda: trn.dual_head_rms_rope(q, k, qw, kw, 1e-6, offset=1000,
@@ -387,6 +397,8 @@ def decode_leg(trn, dev, stream, log):
             for _ in range(3):
                 f()
             torch.cuda.synchronize()
+            if name == "dual_c_abi":
+                continue      # its prepared stream is not the capture stream
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
                 for _ in range(64):
@@ -404,6 +416,8 @@ def decode_leg(trn, dev, stream, log):
                 e1.record(stream)
                 torch.cuda.synchronize()
                 times[name]["eager"].append(e0.elapsed_time(e1) * 1e3 / 200)
+                if name not in graphs:
+                    continue
                 graphs[name].replay()
                 torch.cuda.synchronize()
                 e0.record(stream)
@@ -412,7 +426,7 @@ def decode_leg(trn, dev, stream, log):
                 e1.record(stream)
                 torch.cuda.synchronize()
                 times[name]["graph"].append(e0.elapsed_time(e1) * 1e3 / 640)
-        rec = {n: {m: round(min(v), 2) for m, v in t.items()} for n, t in times.items()}
+        rec = {n: {m: round(min(v), 2) for m, v in t.items() if v} for n, t in times.items()}
         rec["unit"] = "us per call (min over 6 ABBA reps)"
         out[f"tokens_{tokens}"] = rec
         log(f"[bench] decode tokens={tokens}: {rec}")

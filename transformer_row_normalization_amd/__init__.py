@@ -131,22 +131,26 @@ def _stream(t) -> int:
 
 
 def _require(t, name, dtype, device):
-    if t.dtype != dtype:
-        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
-    if t.device != device:
-        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    _check_dev(t, name, dtype, device)
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: ctypes passes it for a c_void_p argument
+    return None if t is None else t.data_ptr()
 
 
 def _check_dev(t, name, dtype, device):
+    # device index comparison (get_device() is -1 on the host); building
+    # torch.device objects costs more than the launch at decode sizes
     if t.dtype != dtype:
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
-    if t.device != device:
+    if device.index is not None:
+        elsewhere = t.get_device() != device.index
+    else:
+        elsewhere = t.device != device
+    if elsewhere:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 

@@ -167,10 +167,45 @@ int rope_candidates(int kind, int dt, int64_t width, bool aligned, int64_t dims,
     return n;
 }
 
+// Candidate lists are a pure function of (kind, type, width, alignment,
+// rotated dims) over an immutable table, so the last few lookups are kept
+// per thread: a decode-size call would otherwise spend most of its host
+// time scanning the table.
+struct CandidateList {
+    int kind = -1, dt = -1;
+    int64_t width = -1, dims = -1;
+    bool aligned = false;
+    int n = 0;
+    const Variant* list[kMaxCandidates];
+};
+
+const CandidateList& cached_candidates(int kind, int dt, int64_t width, bool aligned,
+                                       int64_t dims) {
+    constexpr int kSlots = 8;
+    thread_local CandidateList cache[kSlots];
+    thread_local int next = 0;
+    for (const CandidateList& e : cache)
+        if (e.kind == kind && e.dt == dt && e.width == width && e.aligned == aligned &&
+            e.dims == dims)
+            return e;
+    CandidateList& e = cache[next];
+    next = (next + 1) % kSlots;
+    e.n = (kind == K_ROPE_SPLIT || kind == K_ROPE_TRAD)
+              ? rope_candidates(kind, dt, width, aligned, dims, e.list)
+              : candidates(kind, dt, width, aligned, e.list);
+    e.kind = kind;
+    e.dt = dt;
+    e.width = width;
+    e.aligned = aligned;
+    e.dims = dims;
+    return e;
+}
+
 // Variant index i -> candidate i / 2, persistent grid when i is even.
 bool pick(int kind, int dt, int64_t width, bool aligned, int variant, Choice* c) {
-    const Variant* list[kMaxCandidates];
-    const int n = candidates(kind, dt, width, aligned, list);
+    const CandidateList& cl = cached_candidates(kind, dt, width, aligned, 0);
+    const Variant* const* list = cl.list;
+    const int n = cl.n;
     if (variant < 0) variant = 0;
     if (variant >= 2 * n) return false;
     c->v = list[variant / 2];
@@ -469,8 +504,9 @@ int rope_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
     const int64_t q_rows = tokens * q_heads, k_rows = tokens * k_heads;
     if (q_rows + k_rows == 0) return ok();
     const int kind = traditional ? K_ROPE_TRAD : K_ROPE_SPLIT;
-    const Variant* list[kMaxCandidates];
-    const int n = rope_candidates(kind, dtype, head_dim, al, rope_dims, list);
+    const CandidateList& cl = cached_candidates(kind, dtype, head_dim, al, rope_dims);
+    const Variant* const* list = cl.list;
+    const int n = cl.n;
     if (variant < 0) variant = 0;
     if (variant >= 2 * n)
         return fail(FNORM_ERR_UNSUPPORTED, op,
