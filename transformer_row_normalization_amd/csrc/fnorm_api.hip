@@ -25,7 +25,7 @@
 namespace fnorm {
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0: strided forms, fused RoPE, gated RMSNorm
 
 thread_local char g_err[512];
 
