@@ -32,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -43,11 +44,23 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_bf16_65536x4096_traffic.jso
 KERNEL_SOURCES = ["fnorm_device.hpp", "fnorm_kernels.hpp", "fnorm_instances.hpp", "fnorm_api.hip"]
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments, trailing blanks and empty lines, so
+    that a comment edit does not count as a kernel change.  (String literals
+    containing comment markers are not handled; the kernel sources have
+    none.)"""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the code (comments stripped) of the sources that define the
+    bench's kernels and their launch configuration."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "transformer_row_normalization_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "transformer_row_normalization_amd", "csrc", name)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

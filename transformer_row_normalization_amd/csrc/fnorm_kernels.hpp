@@ -1,11 +1,16 @@
 // Row-normalization kernels for gfx950.
 //
-// Operations (definitions: Emily.Fast API docs, sections `rms_norm` and
-// `layer_norm`; dual form: mlx-c-rust `compile/norm_fusion.rs`):
+// Operations (definitions: Emily.Fast API docs, sections `rms_norm`,
+// `layer_norm`, `rope`; dual form and the gated output norm: mlx-c-rust
+// `compile/norm_fusion.rs`, module docs):
 //   RMSNorm    y = x * rsqrt(mean(x^2) + eps) * w
 //   LayerNorm  y = (x - mean) * rsqrt(var + eps) * w + b   (population var)
 //   dual       RMSNorm of the query head vectors with the query weight and
 //              of the key head vectors with the key weight, one launch.
+//   gated      RMSNorm times SiLU(gate), the gate a second input of x's shape
+//              (OP_RMS_GATED: the RMSNorm kernel with the gate read beside x).
+//   dual+RoPE  the dual form with both outputs rotated before the store
+//              (`dual_rope_rows`, at the end of this file).
 //
 // Resident kernel (`norm_rows`): a row of `width` elements is owned by LPR
 // threads (a lane group inside a wavefront, one wavefront, or LPR/64
@@ -18,7 +23,7 @@
 // over block-rows, so the trip count is uniform inside a block and the
 // barriers of multi-wave rows are never divergent).
 //
-// Arithmetic is fp32 throughout (bf16 inputs widen exactly), with explicit
+// Arithmetic is fp32 throughout (bf16 and fp16 inputs widen exactly), with explicit
 // fmaf where a fused multiply-add is meant; the library is compiled with
 // -ffp-contract=off so no other contraction happens.  LayerNorm takes the
 // mean first and then, from the registers (no second HBM read), the
