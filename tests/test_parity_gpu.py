@@ -321,6 +321,22 @@ def test_large_mean_stability(o):
         helpers.check("layer", y, run_oracle(o, "layer", t, 1e-5), t["w"], f"mean {mean}")
 
 
+def test_magnitude_range(o):
+    """Rows scaled by 1e-15 .. 1e15 (eps > 0 and eps = 0): inside fp32's
+    range for the sum of squares at width 4096 (|x| up to ~2.9e17), every
+    result matches the oracle."""
+    base = inputs.random_rows("layer", 16, 4096, torch.float32, seed=5)
+    for dtype in (torch.float32, torch.bfloat16):
+        for scale in (1e-15, 1e-5, 1e5, 1e15):
+            for eps in (1e-6, 0.0):
+                t = {"x": (base["x"] * scale).to(dtype), "w": base["w"].to(dtype),
+                     "b": (base["b"] * scale).to(dtype)}
+                for op in ("rms", "layer"):
+                    y = run_gpu(op, t, eps)
+                    helpers.check(op, y, run_oracle(o, op, t, eps), t["w"],
+                                  f"{op} scale {scale:g} eps {eps} {dtype}")
+
+
 def test_wide_rows(o):
     for dtype, width in ((torch.float32, 40000), (torch.bfloat16, 70000), (torch.bfloat16, 65537)):
         for op in ("rms", "layer"):
