@@ -88,6 +88,19 @@ __device__ __forceinline__ float silu(float g) {
     return g * (g >= 0.0f ? r : e * r);
 }
 
+// Work order of a workgroup.  Workgroups are dispatched round-robin over the
+// 8 XCDs (workgroup b runs on XCD b % 8, each XCD with its own L2 and
+// address translation); numbering them XCD by XCD gives each XCD one
+// contiguous share of the rows instead of every 8th block-row.  With a
+// persistent grid every XCD still works inside the same window of
+// block-rows; measured on the bench step: 1.5% faster, all three kernels.
+// A permutation of [0, g) whenever g is a multiple of 8; otherwise the
+// hardware order.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_major(unsigned b, unsigned g) {
+    return g % kXcds == 0 ? int64_t(b % kXcds) * (g / kXcds) + b / kXcds : int64_t(b);
+}
+
 // f(0), f(1), ..., f(N-1) with compile-time indices and no loop in the IR.
 // Used for the row stores: a `#pragma unroll` loop of one trip is still a
 // loop when LICM runs, and its store promotion re-creates the store without
