@@ -286,3 +286,13 @@ def test_header_compiles_as_c_and_links(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stderr
     assert "c abi ok" in out.stdout
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without libfnorm.so every entry point raises."""
+    monkeypatch.setattr(trn, "LIB_PATH", str(tmp_path / "absent" / "libfnorm.so"))
+    monkeypatch.setattr(trn, "_lib", None)
+    with pytest.raises(ImportError, match="missing"):
+        trn.lib()
+    with pytest.raises(ImportError):
+        trn.variant_count(trn.OP_RMS, BF16, 128)
