@@ -400,7 +400,8 @@ def decode_leg(trn, dev, stream, log):
       eager  - 200 back-to-back calls between two events: what a host loop
                sustains, launch submission included ("dual_c_abi" calls the
                C entry point directly with prepared arguments, leaving out
-               the Python binding's checks);
+               the Python binding's checks; "dual_prepared" is the binding's
+               own prepared call, `prepare`);
       graph  - one HIP graph holding 64 calls, replayed 10 times: device
                time per call with the host out of the loop."""
     import torch
@@ -421,8 +422,10 @@ def decode_leg(trn, dev, stream, log):
             tokens * qh, tokens * kh, hd, ctypes.c_float(1e-6), trn.BF16,
             ctypes.c_void_p(stream.cuda_stream))
         c_dual = trn.lib().fnorm_dual_head_rms
+        prepared, _ = trn.prepare(trn.dual_head_rms_norm, q, k, qw, kw, 1e-6, q_out=qy, k_out=ky)
         arms = {
             "dual_c_abi": lambda: c_dual(*c_args),
+            "dual_prepared": prepared,
             "two_rms": lambda: (trn.rms_norm(q, qw, 1e-6, out=qy), trn.rms_norm(k, kw, 1e-6, out=ky)),
             "dual": lambda: trn.dual_head_rms_norm(q, k, qw, kw, 1e-6, q_out=qy, k_out=ky),
             "dual_rope": lambda: trn.dual_head_rms_rope(q, k, qw, kw, 1e-6, offset=1000,
@@ -432,8 +435,8 @@ def decode_leg(trn, dev, stream, log):
             for _ in range(3):
                 f()
             torch.cuda.synchronize()
-            if name == "dual_c_abi":
-                continue      # its prepared stream is not the capture stream
+            if name in ("dual_c_abi", "dual_prepared"):
+                continue      # their bound stream is not the capture stream
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
                 for _ in range(64):

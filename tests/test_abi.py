@@ -296,3 +296,11 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         trn.lib()
     with pytest.raises(ImportError):
         trn.variant_count(trn.OP_RMS, BF16, 128)
+
+
+def test_prepare_rejects_host_tensors_and_restores_the_library():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError, match="GPU"):
+        trn.prepare(trn.rms_norm, x, torch.ones(8), 1e-6)
+    assert isinstance(trn.lib(), ctypes.CDLL)      # no recorder left behind

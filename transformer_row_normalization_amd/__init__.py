@@ -13,6 +13,7 @@ missing, every call raises.
   dual_head_rms_norm(q, k, qw, kw, eps)  q/k head RMSNorm in one launch
   dual_head_rms_rope(q, k, qw, kw, eps)  the same, with RoPE fused in
   rms_norm_swiglu(x, g, w, eps)          RMSNorm times SiLU(g), one pass
+  prepare(op, *args)                     validate once, then relaunch cheaply
 Row ops also take row-strided views (e.g. parts of a packed QKV buffer).
 """
 from __future__ import annotations
@@ -20,6 +21,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
+import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfnorm.so")
@@ -80,8 +82,15 @@ _SIGNATURES = {
 }
 
 
+_tls = threading.local()
+
+
 def lib():
-    """The loaded libfnorm.so (raises if it has not been built)."""
+    """The loaded libfnorm.so (raises if it has not been built).  While
+    `prepare` runs an operation, a recorder stands in for it."""
+    rec = getattr(_tls, "recorder", None)
+    if rec is not None:
+        return rec
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
@@ -426,6 +435,75 @@ def bench_copy(src, dst):
     _check(lib().fnorm_bench_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(),
                                   _stream(src)))
     return dst
+
+
+# Entry points that launch work: `prepare` records these; every other
+# entry point (sizes, descriptions) runs for real while it records.
+_LAUNCHES = frozenset(n for n in _SIGNATURES if n.startswith(("fnorm_rms", "fnorm_layer",
+                                                             "fnorm_dual")))
+
+
+class _Recorder:
+    def __init__(self, real):
+        self._real = real
+        self.calls = []
+
+    def __getattr__(self, name):
+        fn = getattr(self._real, name)
+        if name not in _LAUNCHES:
+            return fn
+
+        def record(*args):
+            self.calls.append((fn, args))
+            return 0
+        return record
+
+
+class Prepared:
+    """A validated call with its arguments bound.  Calling it issues the same
+    kernel launch again, on the same tensors and on the stream that was
+    current when it was prepared, through the C entry point directly (no
+    Python-side checks: about 3 us per launch instead of 9).  The tensors
+    must stay alive and keep their storage; their contents may change."""
+
+    __slots__ = ("_calls", "_keep")
+
+    def __init__(self, calls, keep):
+        self._calls = calls
+        self._keep = keep
+
+    def __call__(self):
+        for fn, args in self._calls:
+            status = fn(*args)
+            if status:
+                _check(status)
+
+
+def _as_ctypes(value, ctype):
+    if value is None or isinstance(value, ctypes._SimpleCData):
+        return value
+    return ctype(value)
+
+
+def prepare(op, *args, **kwargs):
+    """Run `op` (rms_norm, layer_norm, dual_head_rms_norm,
+    dual_head_rms_rope or rms_norm_swiglu) once and bind its launch: returns
+    (launch, result), where result is what `op` returned (its outputs,
+    rewritten by every launch()) and launch() repeats the call.  For loops
+    that reuse their buffers, e.g. one decode step per token."""
+    rec = _Recorder(lib())
+    _tls.recorder = rec
+    try:
+        result = op(*args, **kwargs)
+    finally:
+        _tls.recorder = None
+    if not rec.calls:
+        raise ValueError(f"{getattr(op, '__name__', op)} launched nothing to prepare")
+    calls = [(fn, tuple(_as_ctypes(a, t) for a, t in zip(a_s, fn.argtypes)))
+             for fn, a_s in rec.calls]
+    launch = Prepared(calls, (args, kwargs, result))
+    launch()          # the first launch: the library validates the arguments now
+    return launch, result
 
 
 def version() -> int:
