@@ -201,7 +201,8 @@ const CandidateList& cached_candidates(int kind, int dt, int64_t width, bool ali
     return e;
 }
 
-// Variant index i -> candidate i / 2, persistent grid when i is even.
+// Variant index i -> candidate i / 2: its default launch (persistent grid,
+// or a plain grid for grid-first shapes) when i is even, the other when odd.
 bool pick(int kind, int dt, int64_t width, bool aligned, int variant, Choice* c) {
     const CandidateList& cl = cached_candidates(kind, dt, width, aligned, 0);
     const Variant* const* list = cl.list;
@@ -209,7 +210,7 @@ bool pick(int kind, int dt, int64_t width, bool aligned, int variant, Choice* c)
     if (variant < 0) variant = 0;
     if (variant >= 2 * n) return false;
     c->v = list[variant / 2];
-    c->persistent = (variant % 2) == 0;
+    c->persistent = ((variant % 2) == 0) != c->v->grid_first;
     return true;
 }
 

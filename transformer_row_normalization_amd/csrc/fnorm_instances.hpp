@@ -19,6 +19,10 @@ constexpr int op_of() {
                                                       : OP_RMS;
 }
 
+// Grid-cap argument of an exact shape whose default launch is a plain grid
+// (one workgroup per block-row); its persistent form is the other variant.
+constexpr int GRID_FIRST = -1;
+
 template <int KIND, int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, int NT>
 inline Variant make_variant(int cap) {
     constexpr int OP = op_of<KIND>();
@@ -36,17 +40,30 @@ inline Variant make_variant(int cap) {
     v.masked = MASKED;
     v.nt = NT;
     v.wide = false;
-    v.grid_cap = cap;
+    v.grid_cap = cap > 0 ? cap : 0;
+    v.grid_first = cap == GRID_FIRST;
     return v;
 }
 
-template <int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, int NT>
+// Sets of kinds one registration applies to (only those kernels are
+// instantiated): a shape can then sit at a different place in the
+// preference order of LayerNorm and of the RMSNorm family.
+constexpr unsigned KM_LAYER = (1u << K_LAYER) | (1u << K_LAYER_NOBIAS);
+constexpr unsigned KM_RMS_FAMILY = (1u << K_RMS) | (1u << K_DUAL) | (1u << K_RMS_GATED);
+constexpr unsigned KM_ALL = KM_LAYER | KM_RMS_FAMILY;
+
+template <int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, int NT, unsigned KINDS = KM_ALL>
 inline void add_shape(std::vector<Variant>& t, int cap = 0) {
-    t.push_back(make_variant<K_RMS, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
-    t.push_back(make_variant<K_LAYER, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
-    t.push_back(make_variant<K_LAYER_NOBIAS, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
-    t.push_back(make_variant<K_DUAL, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
-    t.push_back(make_variant<K_RMS_GATED, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
+    if constexpr ((KINDS >> K_RMS) & 1u)
+        t.push_back(make_variant<K_RMS, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
+    if constexpr ((KINDS >> K_LAYER) & 1u)
+        t.push_back(make_variant<K_LAYER, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
+    if constexpr ((KINDS >> K_LAYER_NOBIAS) & 1u)
+        t.push_back(make_variant<K_LAYER_NOBIAS, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
+    if constexpr ((KINDS >> K_DUAL) & 1u)
+        t.push_back(make_variant<K_DUAL, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
+    if constexpr ((KINDS >> K_RMS_GATED) & 1u)
+        t.push_back(make_variant<K_RMS_GATED, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
 }
 
 template <int KIND, int DT, int VEC, int BLOCK>
@@ -64,6 +81,7 @@ inline Variant make_wide() {
     v.nt = NT_NONE;
     v.wide = true;
     v.grid_cap = 0;
+    v.grid_first = false;
     return v;
 }
 
@@ -77,9 +95,17 @@ inline void add_wide(std::vector<Variant>& t) {
 
 // Masked shapes for any width up to 8192 packs, used with pack width V
 // (16-byte packs) and with V = 1 (scalar path for misaligned data or widths
-// that are not a multiple of the pack).
+// that are not a multiple of the pack).  The smallest capacity that holds
+// the width serves it.  Rows of 16-byte packs with several packs per lane
+// (the ragged hidden sizes 2560-12288) run 10-18% faster with
+// non-temporal loads and stores on a plain grid than on a full-occupancy
+// persistent grid (measured at bf16 2560, 3072, 3584, 5120, 6144, 7168 and
+// 12288); 640 packs (bf16 5120) get a shape of their own, 6% faster for
+// LayerNorm than the 1024-pack one.
 template <int DT, int V>
 inline void add_masked(std::vector<Variant>& t) {
+    constexpr int WIDE_NT = V > 1 ? NT_BOTH : NT_NONE;
+    constexpr int WIDE_CAP = V > 1 ? GRID_FIRST : 0;
     add_shape<DT, V, 1, 1, 256, true, NT_NONE>(t);
     add_shape<DT, V, 1, 2, 256, true, NT_NONE>(t);
     add_shape<DT, V, 1, 4, 256, true, NT_NONE>(t);
@@ -87,27 +113,36 @@ inline void add_masked(std::vector<Variant>& t) {
     add_shape<DT, V, 1, 16, 256, true, NT_NONE>(t);
     add_shape<DT, V, 1, 32, 256, true, NT_NONE>(t);
     add_shape<DT, V, 1, 64, 256, true, NT_NONE>(t);
-    add_shape<DT, V, 2, 64, 256, true, NT_NONE>(t);
-    add_shape<DT, V, 4, 64, 256, true, NT_NONE>(t);
-    add_shape<DT, V, 8, 64, 256, true, NT_NONE>(t);
-    add_shape<DT, V, 4, 256, 256, true, NT_NONE>(t);
-    add_shape<DT, V, 8, 256, 256, true, NT_NONE>(t);
-    add_shape<DT, V, 4, 1024, 1024, true, NT_NONE>(t);
-    add_shape<DT, V, 8, 1024, 1024, true, NT_NONE>(t);
+    add_shape<DT, V, 2, 64, 256, true, WIDE_NT>(t, WIDE_CAP);
+    add_shape<DT, V, 4, 64, 256, true, WIDE_NT>(t, WIDE_CAP);
+    add_shape<DT, V, 8, 64, 256, true, WIDE_NT>(t, WIDE_CAP);
+    if constexpr (V > 1) add_shape<DT, V, 5, 128, 256, true, WIDE_NT>(t, WIDE_CAP);
+    add_shape<DT, V, 4, 256, 256, true, WIDE_NT>(t, WIDE_CAP);
+    add_shape<DT, V, 8, 256, 256, true, WIDE_NT>(t, WIDE_CAP);
+    add_shape<DT, V, 4, 1024, 1024, true, WIDE_NT>(t, WIDE_CAP);
+    add_shape<DT, V, 8, 1024, 1024, true, WIDE_NT>(t, WIDE_CAP);
 }
 
 // EXACT(VPT, LPR, BLOCK, NT, CAP): an exact shape, its NT_* cache-policy
-// mask, and its persistent-grid cap in workgroups per CU.
+// mask, and its persistent-grid cap in workgroups per CU (0: as many as fit;
+// GRID_FIRST: launch a plain grid by default).
 #define FNORM_EXACT(VPT, LPR, BLOCK, NT, CAP) add_shape<DT, V, VPT, LPR, BLOCK, false, NT>(t, CAP);
+// The same for one set of kinds only.
+#define FNORM_EXACT_FOR(KINDS, VPT, LPR, BLOCK, NT, CAP) \
+    add_shape<DT, V, VPT, LPR, BLOCK, false, NT, KINDS>(t, CAP);
 
-// Preference order, measured on MI355X (cold HBM, bf16, inside the bench
-// step): the first entry of each capacity is the default.  Wide rows win
-// with a small persistent grid (2 workgroups per CU, about 16 KB of rows per
-// workgroup in flight) and non-temporal loads; non-temporal stores pay off
-// for LayerNorm at 4096, not for RMSNorm at 8192 (one 16 KB row per
-// workgroup).  Sub-wave rows (short head vectors) prefer a full-occupancy
-// persistent grid.  Differences under about 3% between cache policies are
-// within the run-to-run spread of these measurements.
+// Preference order, measured on MI355X (cold HBM, 256 MiB inputs, bf16 and
+// fp32): the first entry of each capacity is the default.  Rows of 128 packs
+// and more win with a small persistent grid (2 workgroups per CU) and four
+// to eight packs per lane, so that each wave keeps 4-8 KB of loads in
+// flight: RMSNorm and LayerNorm agree on every shape there.  A grid cap of
+// 3 or 4 is 10-15% slower than 2 at every width measured.  The RMSNorm
+// default at 8192 (one 16 KB row per workgroup, ordinary stores) and the
+// LayerNorm default at 4096 were chosen inside the three-kernel step, where
+// the dirty lines one kernel leaves in the MALL are written back during the
+// next.  Sub-wave rows (short head vectors) prefer a full-occupancy
+// persistent grid, the 96-pack rows a plain grid.  Differences under about
+// 3% between cache policies are within the run-to-run spread.
 template <int DT>
 inline void register_dtype(std::vector<Variant>& t) {
     constexpr int V = 16 / Elem<DT>::bytes;
@@ -124,18 +159,19 @@ inline void register_dtype(std::vector<Variant>& t) {
     FNORM_EXACT(1, 64, 256, NT_LOAD, 0)
     FNORM_EXACT(1, 64, 256, NT_NONE, 0)
     // 96 packs (bf16 768)
-    FNORM_EXACT(3, 32, 256, NT_BOTH, 0)
+    FNORM_EXACT(3, 32, 256, NT_BOTH, GRID_FIRST)
     FNORM_EXACT(3, 32, 256, NT_NONE, 0)
-    // 128 packs (bf16 1024)
+    // 128 packs (bf16 1024, f32 512)
+    FNORM_EXACT(4, 32, 256, NT_BOTH, 2)
     FNORM_EXACT(2, 64, 256, NT_BOTH, 2)
     FNORM_EXACT(2, 64, 256, NT_NONE, 0)
     // 192 packs (f32 768)
     FNORM_EXACT(3, 64, 256, NT_NONE, 0)
     FNORM_EXACT(3, 64, 256, NT_BOTH, 2)
     // 256 packs (f32 1024, bf16 2048)
+    FNORM_EXACT(4, 64, 256, NT_BOTH, 2)
     FNORM_EXACT(2, 128, 256, NT_BOTH, 2)
     FNORM_EXACT(4, 64, 256, NT_NONE, 0)
-    FNORM_EXACT(4, 64, 256, NT_BOTH, 2)
     FNORM_EXACT(1, 256, 256, NT_LOAD, 2)
     // 512 packs (bf16 4096, f32 2048)
     FNORM_EXACT(4, 128, 256, NT_BOTH, 2)
@@ -144,17 +180,21 @@ inline void register_dtype(std::vector<Variant>& t) {
     FNORM_EXACT(2, 256, 256, NT_BOTH, 2)
     FNORM_EXACT(1, 512, 512, NT_LOAD, 2)
     FNORM_EXACT(1, 512, 1024, NT_LOAD, 2)
-    // 1024 packs (bf16 8192, f32 4096)
+    // 1024 packs (bf16 8192, f32 4096): LayerNorm prefers non-temporal
+    // stores (5-7% faster alone); RMSNorm, inside the three-kernel step,
+    // ordinary ones (3% faster step), though non-temporal ones win alone.
+    FNORM_EXACT_FOR(KM_LAYER, 4, 256, 256, NT_BOTH, 2)
+    FNORM_EXACT(4, 256, 256, NT_LOAD, 2)
+    FNORM_EXACT_FOR(KM_RMS_FAMILY, 4, 256, 256, NT_BOTH, 2)
     FNORM_EXACT(1, 1024, 1024, NT_LOAD, 2)
     FNORM_EXACT(1, 1024, 1024, NT_BOTH, 2)
     FNORM_EXACT(1, 1024, 1024, NT_NONE, 2)
     FNORM_EXACT(2, 512, 512, NT_LOAD, 2)
-    FNORM_EXACT(4, 256, 256, NT_LOAD, 2)
     FNORM_EXACT(8, 128, 256, NT_BOTH, 2)
     // 2048 packs (f32 8192, bf16 16384)
+    FNORM_EXACT(8, 256, 256, NT_BOTH, 2)
     FNORM_EXACT(2, 1024, 1024, NT_BOTH, 2)
     FNORM_EXACT(4, 512, 512, NT_BOTH, 2)
-    FNORM_EXACT(8, 256, 256, NT_BOTH, 2)
     add_masked<DT, V>(t);
     add_masked<DT, 1>(t);
     add_wide<DT, V>(t);
@@ -162,5 +202,6 @@ inline void register_dtype(std::vector<Variant>& t) {
 }
 
 #undef FNORM_EXACT
+#undef FNORM_EXACT_FOR
 
 }  // namespace fnorm

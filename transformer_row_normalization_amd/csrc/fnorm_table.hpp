@@ -31,6 +31,7 @@ struct Variant {
     int nt;             // NT_* mask: non-temporal loads of x / stores of y
     bool wide;          // non-resident multi-pass kernel
     int grid_cap;       // persistent grid: workgroups per CU (0 = as many as fit)
+    bool grid_first;    // default launch is one workgroup per block-row, not persistent
     int64_t capacity() const { return wide ? INT64_MAX : int64_t(lpr) * vpt * vec; }
     int rows_per_block() const { return wide ? 1 : block / lpr; }
 };
