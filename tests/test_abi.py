@@ -132,6 +132,38 @@ def test_dispatch_table_choices():
         trn.describe(trn.OP_RMS, BF16, 4096, variant=n)
 
 
+def test_launch_policy_and_per_kind_order():
+    # ragged widths on 16-byte packs default to a plain grid, non-temporal
+    for w in (2560, 3072, 3584, 5120, 6144, 7168, 12288):
+        for op in (trn.OP_RMS, trn.OP_LAYER):
+            d = trn.describe(op, BF16, w)
+            assert ".vec8." in d and ".masked.nt." in d and d.endswith(".grid"), d
+            # the other launch form of the same kernel is the odd variant
+            d1 = trn.describe(op, BF16, w, variant=1)
+            assert d1.rsplit(".", 1)[0] == d.rsplit(".", 1)[0] and ".persistent" in d1, d1
+    assert trn.describe(trn.OP_RMS, BF16, 5120).startswith("rms.bf16.vec8.vpt5.lpr128.")
+    # the 96-pack exact shape (bf16 768) defaults to a plain grid too
+    assert trn.describe(trn.OP_LAYER, BF16, 768).endswith(".exact.nt.grid")
+    # 1024 packs: the same shape, LayerNorm with non-temporal stores first,
+    # the RMSNorm family with ordinary stores first; each list has it once
+    for dt in (BF16, F32):
+        w = 8192 if dt == BF16 else 4096
+        ln = trn.describe(trn.OP_LAYER, dt, w)
+        rms = trn.describe(trn.OP_RMS, dt, w)
+        assert ".vpt4.lpr256.blk256.exact.nt.persistent2" in ln, ln
+        assert ".vpt4.lpr256.blk256.exact.ntld.persistent2" in rms, rms
+        for op in (trn.OP_RMS, trn.OP_LAYER, trn.OP_RMS_SWIGLU):
+            n = trn.variant_count(op, dt, w)
+            names = [trn.describe(op, dt, w, variant=i) for i in range(n)]
+            assert len(set(names)) == n, names
+            assert sum(".vpt4.lpr256.blk256.exact.nt.persistent2" in x for x in names) == 1
+            assert sum(".vpt4.lpr256.blk256.exact.ntld.persistent2" in x for x in names) == 1
+    # 4-8 packs per lane at 128, 256 and 2048 packs
+    assert ".vpt4.lpr32." in trn.describe(trn.OP_LAYER, BF16, 1024)
+    assert ".vpt4.lpr64." in trn.describe(trn.OP_RMS, F32, 1024)
+    assert ".vpt8.lpr256." in trn.describe(trn.OP_LAYER, BF16, 16384)
+
+
 def test_every_resident_width_has_a_kernel():
     for dt, vec in ((F32, 4), (BF16, 8)):
         for w in list(range(1, 300)) + [767, 768, 769, 1023, 1024, 4095, 4096, 8191, 8192]:

@@ -159,7 +159,10 @@ VARIANT_CASES = [("rms", torch.bfloat16, 128), ("rms", torch.bfloat16, 768),
                  ("layer", torch.bfloat16, 2048), ("rms", torch.float32, 8192),
                  ("layer", torch.bfloat16, 100), ("rms", torch.float32, 3),
                  ("rms", torch.float16, 4096), ("layer", torch.float16, 4096),
-                 ("rms", torch.float16, 8192), ("layer", torch.float16, 768)]
+                 ("rms", torch.float16, 8192), ("layer", torch.float16, 768),
+                 ("layer", torch.bfloat16, 5120), ("rms", torch.bfloat16, 2560),
+                 ("layer", torch.float32, 4096), ("rms", torch.float16, 16384),
+                 ("layer", torch.bfloat16, 3584)]
 
 
 @pytest.mark.parametrize("op,dtype,width", VARIANT_CASES,
