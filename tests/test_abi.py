@@ -142,6 +142,13 @@ def test_launch_policy_and_per_kind_order():
             d1 = trn.describe(op, BF16, w, variant=1)
             assert d1.rsplit(".", 1)[0] == d.rsplit(".", 1)[0] and ".persistent" in d1, d1
     assert trn.describe(trn.OP_RMS, BF16, 5120).startswith("rms.bf16.vec8.vpt5.lpr128.")
+    for w in (18432, 24576):
+        d = trn.describe(trn.OP_LAYER, BF16, w)
+        assert d.startswith("layer.bf16.vec8.vpt6.lpr512.blk512.masked.nt.") and d.endswith(".grid"), d
+    # one row per 1024-thread workgroup: persistent first
+    for w in (32768, 40000):
+        d = trn.describe(trn.OP_LAYER, BF16, w)
+        assert ".lpr1024.blk1024.masked.nt." in d and ".persistent" in d, d
     # the 96-pack exact shape (bf16 768) defaults to a plain grid too
     assert trn.describe(trn.OP_LAYER, BF16, 768).endswith(".exact.nt.grid")
     # 1024 packs: the same shape, LayerNorm with non-temporal stores first,

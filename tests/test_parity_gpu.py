@@ -131,7 +131,8 @@ def test_layer_bf16_65536x4096(o):
 # ----------------------------------------------------------------- sweeps
 SWEEP_WIDTHS = [1, 2, 3, 5, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 255,
                 256, 257, 384, 511, 512, 513, 640, 767, 768, 769, 1000, 1023, 1024, 1536, 2047,
-                2048, 2056, 3000, 4095, 4096, 4104, 5120, 8191, 8192, 8200, 12288, 16384]
+                2048, 2056, 3000, 4095, 4096, 4104, 5120, 8191, 8192, 8200, 12288, 16384,
+                18432, 24576, 32768]
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16],
@@ -162,7 +163,8 @@ VARIANT_CASES = [("rms", torch.bfloat16, 128), ("rms", torch.bfloat16, 768),
                  ("rms", torch.float16, 8192), ("layer", torch.float16, 768),
                  ("layer", torch.bfloat16, 5120), ("rms", torch.bfloat16, 2560),
                  ("layer", torch.float32, 4096), ("rms", torch.float16, 16384),
-                 ("layer", torch.bfloat16, 3584)]
+                 ("layer", torch.bfloat16, 3584), ("layer", torch.bfloat16, 18432),
+                 ("rms", torch.float32, 12288)]
 
 
 @pytest.mark.parametrize("op,dtype,width", VARIANT_CASES,

@@ -97,11 +97,14 @@ inline void add_wide(std::vector<Variant>& t) {
 // (16-byte packs) and with V = 1 (scalar path for misaligned data or widths
 // that are not a multiple of the pack).  The smallest capacity that holds
 // the width serves it.  Rows of 16-byte packs with several packs per lane
-// (the ragged hidden sizes 2560-12288) run 10-18% faster with
-// non-temporal loads and stores on a plain grid than on a full-occupancy
-// persistent grid (measured at bf16 2560, 3072, 3584, 5120, 6144, 7168 and
-// 12288); 640 packs (bf16 5120) get a shape of their own, 6% faster for
-// LayerNorm than the 1024-pack one.
+// in 256-thread workgroups (the ragged hidden sizes 2560-12288) run 10-18%
+// faster with non-temporal loads and stores on a plain grid than on a
+// full-occupancy persistent grid (measured at bf16 2560-12288, fp16 3584 and
+// 5120, fp32 2560-6144); 640 packs (bf16 5120) get a shape of their own, 6%
+// faster for LayerNorm than the 1024-pack one, and 2049-3072 packs (bf16
+// 18432, 24576) one of 512 threads, 10% faster for LayerNorm than the
+// 1024-thread shape.  The 1024-thread shapes (one row per workgroup) stay
+// persistent: a plain grid is 6-40% slower there.
 template <int DT, int V>
 inline void add_masked(std::vector<Variant>& t) {
     constexpr int WIDE_NT = V > 1 ? NT_BOTH : NT_NONE;
@@ -119,8 +122,9 @@ inline void add_masked(std::vector<Variant>& t) {
     if constexpr (V > 1) add_shape<DT, V, 5, 128, 256, true, WIDE_NT>(t, WIDE_CAP);
     add_shape<DT, V, 4, 256, 256, true, WIDE_NT>(t, WIDE_CAP);
     add_shape<DT, V, 8, 256, 256, true, WIDE_NT>(t, WIDE_CAP);
-    add_shape<DT, V, 4, 1024, 1024, true, WIDE_NT>(t, WIDE_CAP);
-    add_shape<DT, V, 8, 1024, 1024, true, WIDE_NT>(t, WIDE_CAP);
+    if constexpr (V > 1) add_shape<DT, V, 6, 512, 512, true, WIDE_NT>(t, WIDE_CAP);
+    add_shape<DT, V, 4, 1024, 1024, true, WIDE_NT>(t);
+    add_shape<DT, V, 8, 1024, 1024, true, WIDE_NT>(t);
 }
 
 // EXACT(VPT, LPR, BLOCK, NT, CAP): an exact shape, its NT_* cache-policy
