@@ -201,19 +201,28 @@ def main():
         pairs = [(src_all[i * nbytes_each_way:(i + 1) * nbytes_each_way],
                   dst_all[i * nbytes_each_way:(i + 1) * nbytes_each_way]) for i in range(slices)]
         reps = 20
-        for i in range(3):
-            trn.bench_copy(*pairs[i % slices])
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(reps):
-            trn.bench_copy(*pairs[(i + 3) % slices])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        cms = e0.elapsed_time(e1) / reps
+
+        def timed(copy):
+            for i in range(3):
+                copy(*pairs[i % slices])
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                copy(*pairs[(i + 3) % slices])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        cms = timed(trn.bench_copy)
+        # the runtime's own device-to-device copy (torch's copy_ of two
+        # contiguous byte tensors is a hipMemcpyAsync)
+        mms = timed(lambda s_, d_: d_.copy_(s_))
         return {"kernel": "copy16 (fnorm_bench_copy)", "bytes": 2 * nbytes_each_way,
                 "avg_ms": round(cms, 5), "distinct_slices": slices,
-                "gbs": round(2 * nbytes_each_way / (cms * 1e-3) / 1e9, 1)}
+                "gbs": round(2 * nbytes_each_way / (cms * 1e-3) / 1e9, 1),
+                "d2d_memcpy": {"avg_ms": round(mms, 5),
+                               "gbs": round(2 * nbytes_each_way / (mms * 1e-3) / 1e9, 1)}}
 
     ceiling = None
     if "layer" in ops:
@@ -222,6 +231,10 @@ def main():
             qk = nbytes(dq["q"], dq["k"])
             ceiling["at_dual_bytes"] = copy_ceiling(qk - qk % 16)
         log(f"[bench] copy ceiling: {ceiling}")
+        # each kernel against the copy kernel at (about) its own size
+        for name, op in per_op.items():
+            ref = ceiling.get("at_dual_bytes", ceiling) if name.startswith("dual") else ceiling
+            op["frac_copy"] = round(op["gbs"] / ref["gbs"], 4)
 
     dominant = max(per_op, key=lambda k: per_op[k]["avg_ms"])
     dom = per_op[dominant]
