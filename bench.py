@@ -263,6 +263,21 @@ def main():
     if not args.no_cpu_baseline and len(plan) == 3:
         cpu = cpu_baseline(wl_dual, wl_rms, wl_ln, log)
 
+    # the device as the runtime reports it.  The bus moves bus_bits / 8
+    # bytes per transfer; HBM3E makes four transfers per reported memory
+    # clock (8 Gb/s per pin at 2.0 GHz), so the runtime's figures give
+    # clock * 4 * bus_bits / 8 as peak (the roofline uses the published
+    # 8 TB/s)
+    props = torch.cuda.get_device_properties(dev)
+    mem = trn.device_memory()
+    per_clock = mem["memory_clock_khz"] * 1e3 * mem["memory_bus_bits"] / 8 / 1e9
+    device = {"name": props.name, "arch": props.gcnArchName, **mem,
+              "total_memory_gib": round(props.total_memory / 2**30, 1),
+              "gbs_per_transfer_per_clock": round(per_clock, 1),
+              "props_peak_gbs": round(4 * per_clock, 1),
+              "published_peak_gbs": PEAK_HBM_GBS}
+    log(f"[bench] device: {device}")
+
     out = {"metric": "achieved HBM GB/s (% of peak) and rows/sec for fused RMSNorm/LayerNorm",
            "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -277,7 +292,7 @@ def main():
            "timing": {"value": f"{K} steps between two events on the launch stream",
                       "per_op": f"{K} further steps with an event after every kernel",
                       "ms_per_step_instrumented": round(ms_per_step_instrumented, 5)},
-           "per_op": per_op, "copy_ceiling": ceiling,
+           "device": device, "per_op": per_op, "copy_ceiling": ceiling,
            "roofline": roofline, "cpu_baseline": cpu, "fused_vs_composed": composed,
            "dual_rope": rope, "decode": decode, "rms_swiglu": gated,
            "wall_s_timed_region": round(wall, 4)}

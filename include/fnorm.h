@@ -275,6 +275,15 @@ int fnorm_version(void);
  */
 int fnorm_bench_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
+/*
+ * Measurement aid: what the HIP runtime reports for the current device (the
+ * one hipGetDevice names): its peak memory clock in kHz, its memory bus
+ * width in bits and its compute-unit count.  Any output pointer may be
+ * NULL.  FNORM_ERR_LAUNCH (with the runtime's text in fnorm_last_error())
+ * when the runtime cannot be queried, e.g. with no device.
+ */
+int fnorm_device_memory(int* clock_khz, int* bus_bits, int* compute_units);
+
 #ifdef __cplusplus
 }
 #endif

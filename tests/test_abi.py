@@ -102,6 +102,19 @@ def test_bench_copy_validation(lib):
     assert lib.fnorm_bench_copy(None, B, 64, None) == 1
 
 
+def test_device_memory_query(lib):
+    # with a device: positive figures; without one (this container): a clean
+    # FNORM_ERR_LAUNCH that leaves the outputs alone
+    vals = [ctypes.c_int(-1) for _ in range(3)]
+    rc = lib.fnorm_device_memory(*(ctypes.byref(v) for v in vals))
+    if rc == 0:
+        assert all(v.value > 0 for v in vals)
+    else:
+        assert rc == 7 and all(v.value == -1 for v in vals)
+        assert b"device query failed" in lib.fnorm_last_error()
+    assert lib.fnorm_device_memory(None, None, None) == rc
+
+
 def test_dispatch_table_choices():
     # the default kernels of the hot shapes use 16-byte packs, no predicate
     d = trn.describe(trn.OP_RMS, BF16, 8192)

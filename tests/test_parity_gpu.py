@@ -383,6 +383,12 @@ def test_bench_copy():
     assert torch.equal(src, dst)
 
 
+def test_device_memory():
+    d = trn.device_memory()
+    assert d["memory_clock_khz"] > 0 and d["memory_bus_bits"] > 0
+    assert d["compute_units"] == torch.cuda.get_device_properties(0).multi_processor_count
+
+
 def test_describe_matches_hot_configs():
     assert ".exact" in trn.describe(trn.OP_RMS, trn.BF16, 8192)
     assert ".exact" in trn.describe(trn.OP_LAYER, trn.BF16, 4096)

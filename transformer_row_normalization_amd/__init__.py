@@ -59,6 +59,7 @@ _SIGNATURES = {
     "fnorm_last_error": ([], ctypes.c_char_p),
     "fnorm_version": ([], _I),
     "fnorm_bench_copy": ([_P, _P, _I64, _P], _I),
+    "fnorm_device_memory": ([_P, _P, _P], _I),
     "fnorm_composed_workspace_bytes": ([_I, _I64, _I64], _I64),
     "fnorm_dual_head_rms_rope": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _I64, _I,
                                   _F, _F, _I64, _P, _I, _P], _I),
@@ -504,6 +505,15 @@ def prepare(op, *args, **kwargs):
     launch = Prepared(calls, (args, kwargs, result))
     launch()          # the first launch: the library validates the arguments now
     return launch, result
+
+
+def device_memory() -> dict:
+    """Memory clock (kHz), bus width (bits) and CU count the HIP runtime
+    reports for the current device."""
+    vals = [ctypes.c_int(0) for _ in range(3)]
+    _check(lib().fnorm_device_memory(*(ctypes.byref(v) for v in vals)))
+    return {"memory_clock_khz": vals[0].value, "memory_bus_bits": vals[1].value,
+            "compute_units": vals[2].value}
 
 
 def version() -> int:

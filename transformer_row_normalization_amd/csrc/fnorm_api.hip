@@ -781,6 +781,21 @@ const char* fnorm_last_error(void) { return g_err; }
 
 int fnorm_version(void) { return kVersion; }
 
+int fnorm_device_memory(int* clock_khz, int* bus_bits, int* compute_units) {
+    static const char* op = "fnorm_device_memory";
+    int dev = 0, clock = 0, bus = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&clock, hipDeviceAttributeMemoryClockRate, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&bus, hipDeviceAttributeMemoryBusWidth, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return fail(FNORM_ERR_LAUNCH, op, "device query failed: %s", hipGetErrorString(e));
+    if (clock_khz) *clock_khz = clock;
+    if (bus_bits) *bus_bits = bus;
+    if (compute_units) *compute_units = cus;
+    return ok();
+}
+
 int fnorm_bench_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     static const char* op = "fnorm_bench_copy";
     if (!src || !dst) return fail(FNORM_ERR_NULL, op, "src and dst must be non-NULL");
