@@ -573,7 +573,18 @@ def cpu_baseline(wl_dual, wl_rms, wl_ln, log):
             "kind": "oracle", "seconds": round(dt, 3), "steps": steps,
             "sample": f"{steps} full steps (all rows of the three workloads) through the fp64 C "
                       "oracle, single thread, outputs in 2048-row chunks; same algorithmic bytes",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":
