@@ -288,7 +288,8 @@ def main():
                       "rows_per_step": step_rows, "bytes_per_step": step_bytes,
                       "rows_per_s": round(step_rows / (ms_per_step * 1e-3), 1),
                       "frac_peak_hbm": round(value / PEAK_HBM_GBS, 4),
-                      "parallelism": "rows across workgroups (1 GPU)"},
+                      "parallelism": "rows across workgroups (1 GPU)",
+                      "layer_outliers": int(wl_ln.tensors["outliers"])},
            "timing": {"value": f"{K} steps between two events on the launch stream",
                       "per_op": f"{K} further steps with an event after every kernel",
                       "ms_per_step_instrumented": round(ms_per_step_instrumented, 5)},
