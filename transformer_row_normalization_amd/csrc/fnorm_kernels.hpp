@@ -174,7 +174,8 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
     };
 
     int parity = 0;
-    for (int64_t base = xcd_major(blockIdx.x, gridDim.x) * RPB; base < a.rows;
+    for (int64_t base = xcd_major(blockIdx.x, gridDim.x, (a.rows + RPB - 1) / RPB) * RPB;
+         base < a.rows;
          base += int64_t(gridDim.x) * RPB) {
         const Loc cur = locate(base);
         R xv[VPT];
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(BLOCK) void norm_rows_wide(NormArgs a) {
     const float fwidth = static_cast<float>(width);
     constexpr int64_t STEP = int64_t(BLOCK) * VEC;
 
-    for (int64_t row = xcd_major(blockIdx.x, gridDim.x); row < a.rows; row += gridDim.x) {
+    for (int64_t row = xcd_major(blockIdx.x, gridDim.x, a.rows); row < a.rows; row += gridDim.x) {
         const int64_t off = row * a.xs;
         const int64_t yoff = row * a.ys;
         float s, mean = 0.0f, c = 0.0f;
@@ -479,7 +480,8 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
     __syncthreads();   // inverse frequencies ready; no workgroup barrier after this
 
     const bool small = a.rows <= 0x7fffffff;
-    for (int64_t base = xcd_major(blockIdx.x, gridDim.x) * RPB; base < a.rows;
+    for (int64_t base = xcd_major(blockIdx.x, gridDim.x, (a.rows + RPB - 1) / RPB) * RPB;
+         base < a.rows;
          base += int64_t(gridDim.x) * RPB) {
         // This row's loads are issued first, so their latency overlaps the
         // angle-table phase below.
