@@ -533,10 +533,13 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
             }
             ++k;
         }
-        // the table is written and read by this wavefront only
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        // The table is written and read by this wavefront only, and a
+        // wavefront's LDS operations execute in order: wavefront-scope
+        // fences order them for the compiler and emit no wait (a
+        // workgroup-scope release also waits for the row's HBM load).
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const float2* tab = wtab + leader * ihalf;
         // Split-half, one pack per thread: this lane's (cos, sin) entries are
         // read now, while the row's loads are still in flight.
