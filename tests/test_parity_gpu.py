@@ -463,6 +463,9 @@ ROPE_CASES = [  # (dtype, tokens, q_heads, k_heads, head_dim, dims, traditional,
     (torch.bfloat16, 5, 0, 4, 128, 128, True, 10000.0, 1.0, 9, False),
     (torch.float16, 130, 32, 8, 128, 128, False, 10000.0, 1.0, 2048, False),
     (torch.float16, 40, 4, 4, 64, 64, True, 10000.0, 1.0, 3, False),
+    # head counts that are not powers of two (the token index is a division)
+    (torch.bfloat16, 37, 7, 5, 128, 128, False, 10000.0, 1.0, 77, False),
+    (torch.float32, 19, 40, 10, 64, 64, True, 10000.0, 1.0, 1000, False),
     # long contexts: the angle is formed in fp64 and reduced in turns
     (torch.float32, 24, 4, 2, 128, 128, False, 10000.0, 1.0, 1 << 24, False),
     (torch.bfloat16, 24, 8, 2, 128, 128, True, 1000000.0, 1.0, 1000000, False),

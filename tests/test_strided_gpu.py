@@ -163,6 +163,8 @@ QKV_CASES = [  # (dtype, tokens, q_heads, k_heads, head_dim)
     (torch.float32, 33, 8, 2, 256),
     (torch.bfloat16, 1, 32, 8, 128),
     (torch.bfloat16, 19, 6, 2, 100),       # head_dim that masks
+    (torch.bfloat16, 41, 7, 3, 128),       # head counts that are not powers of two
+    (torch.float32, 23, 40, 5, 64),
 ]
 
 

@@ -483,6 +483,11 @@ int dual_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
     NormArgs a{q, qw_eff, nullptr, qy, k, kw_eff, ky, q_rows + k_rows, q_rows, head_dim, eps,
                qplain ? head_dim : qs, qplain ? head_dim : qys, qplain ? 1 : q_heads,
                kplain ? head_dim : ks, kplain ? head_dim : kys, kplain ? 1 : k_heads};
+    // the kernel divides a row index by the head count only while rows < 2^31
+    if (a.rows <= 0x7fffffff) {
+        if (a.xh > 1) a.xdiv = make_fast_div(uint32_t(a.xh));
+        if (a.x2h > 1) a.x2div = make_fast_div(uint32_t(a.x2h));
+    }
     return launch(op, c, a, stream);
 }
 
@@ -521,7 +526,12 @@ int rope_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
                          head_dim, eps, qs, qys, q_heads > 0 ? q_heads : 1, ks, kys,
                          k_heads > 0 ? k_heads : 1},
                 q_heads > 0 ? q_heads : 1, k_heads > 0 ? k_heads : 1, rope_dims, offset, base,
-                scale, freqs};
+                scale, freqs, FastDiv{}, FastDiv{}};
+    // the kernel divides by the head counts only while rows < 2^31
+    if (ra.n.rows <= 0x7fffffff) {
+        ra.qdiv = make_fast_div(uint32_t(ra.q_heads));
+        ra.kdiv = make_fast_div(uint32_t(ra.k_heads));
+    }
     const int64_t lds = rope_lds_bytes(*v, rope_dims);
     const int64_t rpb = v->rows_per_block();
     int64_t grid = (ra.n.rows + rpb - 1) / rpb;
