@@ -407,6 +407,7 @@ int rows_impl(const char* op, int fop, const void* x, int64_t xs, const void* g,
     NormArgs a{x,    w,    b,     y,     nullptr, nullptr, nullptr, rows, rows, width,
                eps,  one ? width : xs, one ? width : ys, 1, width, width, 1,
                gated ? g : nullptr, one ? width : gs};
+    a.inv_width = 1.0f / static_cast<float>(width);
     return launch(op, c, a, stream);
 }
 
@@ -488,6 +489,7 @@ int dual_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
         if (a.xh > 1) a.xdiv = make_fast_div(uint32_t(a.xh));
         if (a.x2h > 1) a.x2div = make_fast_div(uint32_t(a.x2h));
     }
+    a.inv_width = 1.0f / static_cast<float>(head_dim);
     return launch(op, c, a, stream);
 }
 
@@ -527,6 +529,7 @@ int rope_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
                          k_heads > 0 ? k_heads : 1},
                 q_heads > 0 ? q_heads : 1, k_heads > 0 ? k_heads : 1, rope_dims, offset, base,
                 scale, freqs, FastDiv{}, FastDiv{}};
+    ra.n.inv_width = 1.0f / static_cast<float>(head_dim);
     // the kernel divides by the head counts only while rows < 2^31
     if (ra.n.rows <= 0x7fffffff) {
         ra.qdiv = make_fast_div(uint32_t(ra.q_heads));

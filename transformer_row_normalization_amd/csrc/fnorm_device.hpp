@@ -220,10 +220,12 @@ __device__ __forceinline__ void keep_packed(R (&p)[N]) {
 }
 
 // ---------------------------------------------------------------- reductions
+// v moved across lanes by a DPP control.  A lane whose source lies outside
+// its row reads 0 (bound_ctrl), so no register has to be cleared first.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 // DPP controls (GFX9 encoding): quad permutes, and the in-row mirrors.
