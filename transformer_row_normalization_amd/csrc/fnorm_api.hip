@@ -493,6 +493,26 @@ int dual_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
     return launch(op, c, a, stream);
 }
 
+// Workgroups of the query and key segments of a dual launch over qu and ku
+// block-rows: one per block-row (a plain grid), or, when that is more than
+// `cap` (> 0: a persistent grid), `cap` shared in proportion to the
+// block-rows, the query share a multiple of 8 so that both segments keep the
+// XCD-major order.  A segment with rows always gets a workgroup.
+void split_grid(int64_t qu, int64_t ku, int64_t cap, int64_t* gq, int64_t* gk) {
+    constexpr int64_t kMaxSegment = int64_t(1) << 29;   // grid-stride loops cover the rest
+    int64_t q = qu, k = ku;
+    if (cap > 0 && qu + ku > cap) {
+        q = ku > 0 ? cap * qu / (qu + ku) : cap;
+        if (ku > 0 && q >= kXcds) q -= q % kXcds;
+        if (qu > 0 && q < 1) q = 1;
+        if (q > qu) q = qu;
+        k = ku > 0 ? (cap - q > 1 ? cap - q : 1) : 0;
+        if (k > ku) k = ku;
+    }
+    *gq = q < kMaxSegment ? q : kMaxSegment;
+    *gk = k < kMaxSegment ? k : kMaxSegment;
+}
+
 int rope_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t ks,
               const void* qw, const void* kw, void* qy, int64_t qys, void* ky, int64_t kys,
               int64_t tokens, int64_t q_heads, int64_t k_heads, int64_t head_dim, float eps,
@@ -528,7 +548,7 @@ int rope_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
                          head_dim, eps, qs, qys, q_heads > 0 ? q_heads : 1, ks, kys,
                          k_heads > 0 ? k_heads : 1},
                 q_heads > 0 ? q_heads : 1, k_heads > 0 ? k_heads : 1, rope_dims, offset, base,
-                scale, freqs, FastDiv{}, FastDiv{}};
+                scale, freqs, FastDiv{}, FastDiv{}, 0u};
     ra.n.inv_width = 1.0f / static_cast<float>(head_dim);
     // the kernel divides by the head counts only while rows < 2^31
     if (ra.n.rows <= 0x7fffffff) {
@@ -537,13 +557,12 @@ int rope_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
     }
     const int64_t lds = rope_lds_bytes(*v, rope_dims);
     const int64_t rpb = v->rows_per_block();
-    int64_t grid = (ra.n.rows + rpb - 1) / rpb;
-    if (persistent) {
-        const int per_cu = blocks_per_cu_lds(v, lds);
-        const int64_t cap = int64_t(device_cus()) * per_cu;
-        if (grid > cap) grid = cap;
-    }
-    if (grid > (int64_t(1) << 30)) grid = int64_t(1) << 30;
+    const int64_t cap =
+        persistent ? int64_t(device_cus()) * blocks_per_cu_lds(v, lds) : int64_t(0);
+    int64_t gq = 0, gk = 0;
+    split_grid((q_rows + rpb - 1) / rpb, (k_rows + rpb - 1) / rpb, cap, &gq, &gk);
+    ra.q_blocks = uint32_t(gq);
+    const int64_t grid = gq + gk;
     void* args[] = {&ra};
     hipError_t e = hipLaunchKernel(v->fn, dim3(unsigned(grid)), dim3(unsigned(v->block)), args,
                                    size_t(lds), static_cast<hipStream_t>(stream));

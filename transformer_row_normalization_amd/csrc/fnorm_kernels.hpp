@@ -438,6 +438,7 @@ struct RopeArgs {
     float scale;
     const float* freqs;  // dims/2 inverse frequencies, or null
     FastDiv qdiv, kdiv;  // division by q_heads / k_heads (rows < 2^31)
+    uint32_t q_blocks;   // workgroups [0, q_blocks) serve the queries, the rest the keys
 };
 
 template <int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, int NT, bool TRAD>
@@ -456,8 +457,24 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
     const int wave_lane = tid & 63;
     const int64_t width = a.width;
     const float inv_width = a.inv_width;
-    const int64_t last = a.rows - 1;
     const int64_t half = ra.dims / 2;
+
+    // The grid is split in two segments: workgroups [0, q_blocks) serve the
+    // query rows, the others the key rows.  A workgroup's tensor is then a
+    // uniform choice, so its pointers, strides, head count and weight are
+    // scalars, not per-lane selects, and rows are counted within the tensor.
+    const bool second = blockIdx.x >= ra.q_blocks;
+    const unsigned seg_block = second ? blockIdx.x - ra.q_blocks : blockIdx.x;
+    const unsigned seg_grid = second ? gridDim.x - ra.q_blocks : ra.q_blocks;
+    const int64_t seg_rows = second ? a.rows - a.rows1 : a.rows1;
+    const int64_t last = seg_rows - 1;
+    const void* const xp = second ? a.x2 : a.x;
+    void* const yp = second ? a.y2 : a.y;
+    const void* const wp = second ? a.w2 : a.w;
+    const int64_t xs = second ? a.x2s : a.xs;
+    const int64_t ys = second ? a.y2s : a.ys;
+    const int64_t den = second ? ra.k_heads : ra.q_heads;
+    const FastDiv hdiv = second ? ra.kdiv : ra.qdiv;
     double* invf = rope_smem;
     float2* cs = reinterpret_cast<float2*>(rope_smem + half);
 
@@ -483,33 +500,26 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
     float2* wtab = cs + int64_t(wave) * W * half;
     const int ihalf = static_cast<int>(half);
 
-    R wv[VPT], wv2[VPT];
+    R wv[VPT];
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-        wv[v] = in_row(v) ? load_raw<DT, VEC, false>(a.w, col_of(v)) : raw_zero<DT, VEC>();
-        wv2[v] = in_row(v) ? load_raw<DT, VEC, false>(a.w2, col_of(v)) : raw_zero<DT, VEC>();
-    }
+    for (int v = 0; v < VPT; ++v)
+        wv[v] = in_row(v) ? load_raw<DT, VEC, false>(wp, col_of(v)) : raw_zero<DT, VEC>();
     __syncthreads();   // inverse frequencies ready; no workgroup barrier after this
 
     const bool small = a.rows <= 0x7fffffff;
-    for (int64_t base = xcd_major(blockIdx.x, gridDim.x, (a.rows + RPB - 1) / RPB) * RPB;
-         base < a.rows;
-         base += int64_t(gridDim.x) * RPB) {
+    for (int64_t base = xcd_major(seg_block, seg_grid, (seg_rows + RPB - 1) / RPB) * RPB;
+         base < seg_rows;
+         base += int64_t(seg_grid) * RPB) {
         // This row's loads are issued first, so their latency overlaps the
         // angle-table phase below.
         const bool valid = base + group <= last;
-        const int64_t row = valid ? base + group : last;
-        const bool second = row >= a.rows1;
-        const void* xp = second ? a.x2 : a.x;
-        void* yp = second ? a.y2 : a.y;
-        // token of this row (heads of a token are consecutive rows)
-        const int64_t num = second ? row - a.rows1 : row;
-        const int64_t den = second ? ra.k_heads : ra.q_heads;
-        const int64_t tok =
-            small ? int64_t((second ? ra.kdiv : ra.qdiv).div(uint32_t(num))) : num / den;
+        // row of this tensor; its token (the heads of a token are
+        // consecutive rows) and head
+        const int64_t num = valid ? base + group : last;
+        const int64_t tok = small ? int64_t(hdiv.div(uint32_t(num))) : num / den;
         const int64_t head = num - tok * den;
-        const int64_t xo = tok * (second ? a.x2s : a.xs) + head * width;
-        const int64_t yo = tok * (second ? a.y2s : a.ys) + head * width;
+        const int64_t xo = tok * xs + head * width;
+        const int64_t yo = tok * ys + head * width;
         R xv[VPT];
 #pragma unroll
         for (int v = 0; v < VPT; ++v)
@@ -518,7 +528,7 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
 
         // Its position, and the first slot of this wavefront holding the
         // same token (the slot that owns the table).
-        const int64_t first = (second ? a.rows1 : 0) + tok * den;
+        const int64_t first = tok * den;
         const int64_t wave_row0 = base + int64_t(wave) * W;
         const int leader = first > wave_row0 ? int(first - wave_row0) : 0;
         const double pos = static_cast<double>(ra.offset + tok) * static_cast<double>(ra.scale);
@@ -579,7 +589,7 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
         float o[VPT][VEC];
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
-            const R wr = second ? wv2[v] : wv[v];
+            const R wr = wv[v];
 #pragma unroll
             for (int i = 0; i < VEC; ++i)
                 o[v][i] = (elem<DT, VEC>(xv[v], i) * scale) * elem<DT, VEC>(wr, i);
