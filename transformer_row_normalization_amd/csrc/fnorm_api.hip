@@ -310,16 +310,39 @@ int blocks_per_cu_lds(const Variant* v, int64_t lds) {
     return n;
 }
 
+// Workgroups of the query and key segments of a dual launch over qu and ku
+// block-rows: one per block-row (a plain grid), or, when that is more than
+// `cap` (> 0: a persistent grid), `cap` shared in proportion to the
+// block-rows, the query share a multiple of 8 so that both segments keep the
+// XCD-major order.  A segment with rows always gets a workgroup.
+void split_grid(int64_t qu, int64_t ku, int64_t cap, int64_t* gq, int64_t* gk) {
+    constexpr int64_t kMaxSegment = int64_t(1) << 29;   // grid-stride loops cover the rest
+    int64_t q = qu, k = ku;
+    if (cap > 0 && qu + ku > cap) {
+        q = ku > 0 ? cap * qu / (qu + ku) : cap;
+        if (ku > 0 && q >= kXcds) q -= q % kXcds;
+        if (qu > 0 && q < 1) q = 1;
+        if (q > qu) q = qu;
+        k = ku > 0 ? (cap - q > 1 ? cap - q : 1) : 0;
+        if (k > ku) k = ku;
+    }
+    *gq = q < kMaxSegment ? q : kMaxSegment;
+    *gk = k < kMaxSegment ? k : kMaxSegment;
+}
+
 int launch(const char* op, const Choice& c, NormArgs& a, void* stream) {
     const int64_t rpb = c.v->rows_per_block();
-    const int64_t needed = (a.rows + rpb - 1) / rpb;
-    int64_t grid = needed;
+    int64_t cap = 0;
     if (c.persistent) {
         int per_cu = blocks_per_cu(c.v);
         if (c.v->grid_cap > 0 && c.v->grid_cap < per_cu) per_cu = c.v->grid_cap;
-        const int64_t cap = int64_t(device_cus()) * per_cu;
-        if (grid > cap) grid = cap;
+        cap = int64_t(device_cus()) * per_cu;
     }
+    // work units: block-rows (a dual launch's two tensors do not share one)
+    int64_t grid = c.v->kind == K_DUAL
+                       ? (a.rows1 + rpb - 1) / rpb + (a.rows - a.rows1 + rpb - 1) / rpb
+                       : (a.rows + rpb - 1) / rpb;
+    if (cap > 0 && grid > cap) grid = cap;
     if (grid > (int64_t(1) << 30)) grid = int64_t(1) << 30;  // grid-stride covers the rest
     void* args[] = {&a};
     hipError_t e = hipLaunchKernel(c.v->fn, dim3(unsigned(grid)), dim3(unsigned(c.v->block)),
@@ -491,26 +514,6 @@ int dual_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
     }
     a.inv_width = 1.0f / static_cast<float>(head_dim);
     return launch(op, c, a, stream);
-}
-
-// Workgroups of the query and key segments of a dual launch over qu and ku
-// block-rows: one per block-row (a plain grid), or, when that is more than
-// `cap` (> 0: a persistent grid), `cap` shared in proportion to the
-// block-rows, the query share a multiple of 8 so that both segments keep the
-// XCD-major order.  A segment with rows always gets a workgroup.
-void split_grid(int64_t qu, int64_t ku, int64_t cap, int64_t* gq, int64_t* gk) {
-    constexpr int64_t kMaxSegment = int64_t(1) << 29;   // grid-stride loops cover the rest
-    int64_t q = qu, k = ku;
-    if (cap > 0 && qu + ku > cap) {
-        q = ku > 0 ? cap * qu / (qu + ku) : cap;
-        if (ku > 0 && q >= kXcds) q -= q % kXcds;
-        if (qu > 0 && q < 1) q = 1;
-        if (q > qu) q = qu;
-        k = ku > 0 ? (cap - q > 1 ? cap - q : 1) : 0;
-        if (k > ku) k = ku;
-    }
-    *gq = q < kMaxSegment ? q : kMaxSegment;
-    *gk = k < kMaxSegment ? k : kMaxSegment;
 }
 
 int rope_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t ks,

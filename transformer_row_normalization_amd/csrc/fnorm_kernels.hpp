@@ -115,7 +115,16 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
     const int lane = tid % LPR;
     const int64_t width = a.width;
     const float inv_width = a.inv_width;
-    const int64_t last = a.rows - 1;
+
+    // Work units are block-rows of RPB rows.  A dual launch numbers the
+    // first tensor's (queries) units before the second's (keys), so no unit
+    // holds rows of both: the tensor of a unit is uniform over the
+    // workgroup, its pointers and strides are scalars, and rows are counted
+    // within the tensor.  One grid-stride loop covers all units, so the
+    // work per workgroup stays as even as with a single tensor.
+    const int64_t units1 = DUAL ? (a.rows1 + RPB - 1) / RPB : 0;
+    const int64_t units = DUAL ? units1 + (a.rows - a.rows1 + RPB - 1) / RPB
+                               : (a.rows + RPB - 1) / RPB;
 
     // Column of pack v of this thread, and whether it lies inside the row.
     auto col_of = [&](int v) { return int64_t(v * LPR + lane) * VEC; };
@@ -138,28 +147,21 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
     // predicate) and store nothing.  (Issuing the next block-row's loads
     // before this row's reductions measured slower on every bench shape.)
     struct Loc {
-        bool valid, second;
+        bool valid, second;   // second: uniform over the workgroup
         const void* xp;
         void* yp;
         RowOff off;
         int64_t goff;
     };
-    auto locate = [&](int64_t base) {
+    auto locate = [&](int64_t unit) {
         Loc L;
+        L.second = DUAL && unit >= units1;
+        const int64_t base = (L.second ? unit - units1 : unit) * RPB;
+        const int64_t last = (DUAL ? (L.second ? a.rows - a.rows1 : a.rows1) : a.rows) - 1;
         L.valid = base + group <= last;
-        const int64_t row = L.valid ? base + group : last;
-        L.xp = a.x;
-        L.yp = a.y;
-        L.second = false;
-        int64_t r = row;
-        if constexpr (DUAL) {
-            L.second = row >= a.rows1;
-            if (L.second) {
-                L.xp = a.x2;
-                L.yp = a.y2;
-                r = row - a.rows1;
-            }
-        }
+        const int64_t r = L.valid ? base + group : last;   // row of this tensor
+        L.xp = L.second ? a.x2 : a.x;
+        L.yp = L.second ? a.y2 : a.y;
         L.off = L.second ? row_offsets(r, a.x2h, a.x2div, a.x2s, a.y2s, width)
                          : row_offsets(r, a.xh, a.xdiv, a.xs, a.ys, width);
         L.goff = GATED ? r * a.gs : 0;
@@ -179,10 +181,9 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
     };
 
     int parity = 0;
-    for (int64_t base = xcd_major(blockIdx.x, gridDim.x, (a.rows + RPB - 1) / RPB) * RPB;
-         base < a.rows;
-         base += int64_t(gridDim.x) * RPB) {
-        const Loc cur = locate(base);
+    for (int64_t unit = xcd_major(blockIdx.x, gridDim.x, units); unit < units;
+         unit += gridDim.x) {
+        const Loc cur = locate(unit);
         R xv[VPT];
         load_row(cur, xv);
         R gv[GATED ? VPT : 1];
