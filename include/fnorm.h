@@ -222,6 +222,9 @@ int fnorm_variant_count(int op, int dtype, int64_t width, int aligned);
  * Writes into buf (NUL-terminated, at most len bytes) the name of the kernel
  * and launch shape that variant `variant` (-1 = default) of (op, dtype,
  * width, aligned) uses, e.g. "rms.bf16.vec8.vpt4.lpr256.blk256.exact.persistent".
+ * The last field is the launch: "persistent" (as many workgroups as fit),
+ * "persistentK" (K workgroups per CU), "grid" (one workgroup per block of
+ * rows) or "gridK" (the same, with at most K workgroups resident per CU).
  * Returns FNORM_OK, FNORM_ERR_UNSUPPORTED or FNORM_ERR_NULL.  Host-only.
  */
 int fnorm_describe(int op, int dtype, int64_t width, int aligned, int variant, char* buf,

@@ -147,21 +147,30 @@ def test_dispatch_table_choices():
 
 def test_launch_policy_and_per_kind_order():
     # ragged widths on 16-byte packs default to a plain grid, non-temporal
-    for w in (2560, 3072, 3584, 5120, 6144, 7168, 12288):
+    # with at most 3-4 workgroups resident per CU (".gridK")
+    expect = {2560: 3, 3072: 3, 3584: 3, 5120: 3, 6144: 4, 7168: 4, 12288: 3}
+    for w, k in expect.items():
         for op in (trn.OP_RMS, trn.OP_LAYER):
             d = trn.describe(op, BF16, w)
-            assert ".vec8." in d and ".masked.nt." in d and d.endswith(".grid"), d
+            assert ".vec8." in d and ".masked.nt." in d and d.endswith(f".grid{k}"), d
             # the other launch form of the same kernel is the odd variant
             d1 = trn.describe(op, BF16, w, variant=1)
             assert d1.rsplit(".", 1)[0] == d.rsplit(".", 1)[0] and ".persistent" in d1, d1
     assert trn.describe(trn.OP_RMS, BF16, 5120).startswith("rms.bf16.vec8.vpt5.lpr128.")
+    # the shortest masked rows run without a limit
+    assert trn.describe(trn.OP_RMS, BF16, 640).endswith(".masked.nt.grid")
     for w in (18432, 24576):
         d = trn.describe(trn.OP_LAYER, BF16, w)
-        assert d.startswith("layer.bf16.vec8.vpt6.lpr512.blk512.masked.nt.") and d.endswith(".grid"), d
+        assert d.startswith("layer.bf16.vec8.vpt6.lpr512.blk512.masked.nt.") and d.endswith(".grid2"), d
     # one row per 1024-thread workgroup: persistent first
     for w in (32768, 40000):
-        d = trn.describe(trn.OP_LAYER, BF16, w)
+        d = trn.describe(trn.OP_RMS, BF16, w)
         assert ".lpr1024.blk1024.masked.nt." in d and ".persistent" in d, d
+    assert ".vpt4.lpr1024.blk1024.masked.nt.persistent" in trn.describe(trn.OP_LAYER, BF16, 32768)
+    # LayerNorm with a bias at 4097-8192 packs: 16 packs per lane, 512 threads
+    for dt, w in ((BF16, 40000), (BF16, 65536), (F32, 32768)):
+        d = trn.describe(trn.OP_LAYER, dt, w)
+        assert ".vpt16.lpr512.blk512.masked.nt.persistent" in d, d
     # the 96-pack exact shape (bf16 768) defaults to a plain grid too
     assert trn.describe(trn.OP_LAYER, BF16, 768).endswith(".exact.nt.grid")
     # 1024 packs: the same shape, LayerNorm with non-temporal stores first,

@@ -47,6 +47,7 @@ int ok() {
 struct Registry {
     std::vector<Variant> table;
     std::unique_ptr<std::atomic<int>[]> occupancy;  // blocks per CU, 0 = not yet queried
+    std::unique_ptr<std::atomic<int>[]> grid_lds;   // resident-limit LDS, -1 = not yet set
 };
 
 const Registry& registry() {
@@ -57,7 +58,11 @@ const Registry& registry() {
         register_f16(reg.table);
         register_rope(reg.table);
         reg.occupancy.reset(new std::atomic<int>[reg.table.size()]);
-        for (size_t i = 0; i < reg.table.size(); ++i) reg.occupancy[i].store(0);
+        reg.grid_lds.reset(new std::atomic<int>[reg.table.size()]);
+        for (size_t i = 0; i < reg.table.size(); ++i) {
+            reg.occupancy[i].store(0);
+            reg.grid_lds[i].store(-1);
+        }
         return reg;
     }();
     return r;
@@ -234,6 +239,10 @@ void describe_choice(const Choice& c, char* buf, size_t len) {
         std::snprintf(buf, len, "%s.%s.vec%d.vpt%d.lpr%d.blk%d.%s%s.persistent%d", kinds[v.kind],
                       dtype_name(v.dt), v.vec, v.vpt, v.lpr, v.block,
                       v.masked ? "masked" : "exact", nt, v.grid_cap);
+    else if (!c.persistent && v.grid_resident > 0)
+        std::snprintf(buf, len, "%s.%s.vec%d.vpt%d.lpr%d.blk%d.%s%s.grid%d", kinds[v.kind],
+                      dtype_name(v.dt), v.vec, v.vpt, v.lpr, v.block,
+                      v.masked ? "masked" : "exact", nt, v.grid_resident);
     else
         std::snprintf(buf, len, "%s.%s.vec%d.vpt%d.lpr%d.blk%d.%s%s.%s", kinds[v.kind],
                       dtype_name(v.dt), v.vec, v.vpt, v.lpr, v.block,
@@ -310,6 +319,35 @@ int blocks_per_cu_lds(const Variant* v, int64_t lds) {
     return n;
 }
 
+// Dynamic LDS per workgroup that holds a plain grid of `v` to at most
+// k = v->grid_resident workgroups per CU: each reserves LDS_per_CU / (k + 1/2)
+// bytes in all (its own LDS included), so k fit and k + 1 do not.  0 when the
+// kernel's registers already hold it to k or fewer, or when the device cannot
+// grant the reservation (then the grid runs unlimited).  Cached per variant.
+int resident_lds(const Variant* v) {
+    const Registry& r = registry();
+    std::atomic<int>& slot = r.grid_lds[v - r.table.data()];
+    int bytes = slot.load(std::memory_order_relaxed);
+    if (bytes >= 0) return bytes;
+    bytes = 0;
+    const int k = v->grid_resident;
+    int dev = 0, per_cu = 0, per_block = 0;
+    hipFuncAttributes fa{};
+    if (k > 0 && blocks_per_cu(v) > k && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                              dev) == hipSuccess &&
+        hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) ==
+            hipSuccess &&
+        hipFuncGetAttributes(&fa, v->fn) == hipSuccess) {
+        const int64_t total = 2 * int64_t(per_cu) / (2 * k + 1);
+        const int64_t dyn = total - int64_t(fa.sharedSizeBytes);
+        if (dyn > 0 && total <= per_block && blocks_per_cu_lds(v, dyn) <= k)
+            bytes = int(dyn);
+    }
+    slot.store(bytes, std::memory_order_relaxed);
+    return bytes;
+}
+
 // Workgroups of the query and key segments of a dual launch over qu and ku
 // block-rows: one per block-row (a plain grid), or, when that is more than
 // `cap` (> 0: a persistent grid), `cap` shared in proportion to the
@@ -344,9 +382,10 @@ int launch(const char* op, const Choice& c, NormArgs& a, void* stream) {
                        : (a.rows + rpb - 1) / rpb;
     if (cap > 0 && grid > cap) grid = cap;
     if (grid > (int64_t(1) << 30)) grid = int64_t(1) << 30;  // grid-stride covers the rest
+    const int lds = !c.persistent && c.v->grid_resident > 0 ? resident_lds(c.v) : 0;
     void* args[] = {&a};
     hipError_t e = hipLaunchKernel(c.v->fn, dim3(unsigned(grid)), dim3(unsigned(c.v->block)),
-                                   args, 0, static_cast<hipStream_t>(stream));
+                                   args, size_t(lds), static_cast<hipStream_t>(stream));
     hipError_t e2 = hipGetLastError();
     if (e == hipSuccess) e = e2;
     if (e != hipSuccess)

@@ -66,6 +66,18 @@ __device__ __forceinline__ typename Raw<DT, VEC>::type load_raw(const void* base
     else return *p;
 }
 
+// Load the pack `off` bytes past `row`.  The 32-bit offset lets the compiler
+// address each pack as one 64-bit row base plus a 32-bit lane offset (a
+// scalar base when the row is uniform over the workgroup), so a lane keeps
+// one register per pack offset instead of a 64-bit address per pack.
+template <int DT, int VEC, bool NT>
+__device__ __forceinline__ typename Raw<DT, VEC>::type load_at(const char* row, uint32_t off) {
+    using R = typename Raw<DT, VEC>::type;
+    const R* p = reinterpret_cast<const R*>(row + off);
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
 // SiLU(g) = g * sigmoid(g) in fp32, in a form that cannot overflow:
 // e = exp(-|g|) lies in (0, 1], sigmoid(|g|) = 1 / (1 + e), and
 // sigmoid(-|g|) = e / (1 + e).  e comes from the hardware base-2
@@ -143,6 +155,15 @@ template <int DT, int VEC, bool NT>
 __device__ __forceinline__ void store_raw(void* base, int64_t idx, typename Raw<DT, VEC>::type v) {
     using R = typename Raw<DT, VEC>::type;
     R* p = reinterpret_cast<R*>(static_cast<char*>(base) + idx * Elem<DT>::bytes);
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// Store counterpart of load_at.
+template <int DT, int VEC, bool NT>
+__device__ __forceinline__ void store_at(char* row, uint32_t off, typename Raw<DT, VEC>::type v) {
+    using R = typename Raw<DT, VEC>::type;
+    R* p = reinterpret_cast<R*>(row + off);
     if constexpr (NT) __builtin_nontemporal_store(v, p);
     else *p = v;
 }

@@ -24,7 +24,7 @@ constexpr int op_of() {
 constexpr int GRID_FIRST = -1;
 
 template <int KIND, int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, int NT>
-inline Variant make_variant(int cap) {
+inline Variant make_variant(int cap, int resident) {
     constexpr int OP = op_of<KIND>();
     constexpr bool BIAS = KIND == K_LAYER;
     constexpr bool DUAL = KIND == K_DUAL;
@@ -42,28 +42,30 @@ inline Variant make_variant(int cap) {
     v.wide = false;
     v.grid_cap = cap > 0 ? cap : 0;
     v.grid_first = cap == GRID_FIRST;
+    v.grid_resident = resident;
     return v;
 }
 
 // Sets of kinds one registration applies to (only those kernels are
 // instantiated): a shape can then sit at a different place in the
 // preference order of LayerNorm and of the RMSNorm family.
-constexpr unsigned KM_LAYER = (1u << K_LAYER) | (1u << K_LAYER_NOBIAS);
+constexpr unsigned KM_LAYER_BIAS = 1u << K_LAYER;
+constexpr unsigned KM_LAYER = KM_LAYER_BIAS | (1u << K_LAYER_NOBIAS);
 constexpr unsigned KM_RMS_FAMILY = (1u << K_RMS) | (1u << K_DUAL) | (1u << K_RMS_GATED);
 constexpr unsigned KM_ALL = KM_LAYER | KM_RMS_FAMILY;
 
 template <int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, int NT, unsigned KINDS = KM_ALL>
-inline void add_shape(std::vector<Variant>& t, int cap = 0) {
+inline void add_shape(std::vector<Variant>& t, int cap = 0, int resident = 0) {
     if constexpr ((KINDS >> K_RMS) & 1u)
-        t.push_back(make_variant<K_RMS, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
+        t.push_back(make_variant<K_RMS, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap, resident));
     if constexpr ((KINDS >> K_LAYER) & 1u)
-        t.push_back(make_variant<K_LAYER, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
+        t.push_back(make_variant<K_LAYER, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap, resident));
     if constexpr ((KINDS >> K_LAYER_NOBIAS) & 1u)
-        t.push_back(make_variant<K_LAYER_NOBIAS, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
+        t.push_back(make_variant<K_LAYER_NOBIAS, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap, resident));
     if constexpr ((KINDS >> K_DUAL) & 1u)
-        t.push_back(make_variant<K_DUAL, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
+        t.push_back(make_variant<K_DUAL, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap, resident));
     if constexpr ((KINDS >> K_RMS_GATED) & 1u)
-        t.push_back(make_variant<K_RMS_GATED, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap));
+        t.push_back(make_variant<K_RMS_GATED, DT, VEC, VPT, LPR, BLOCK, MASKED, NT>(cap, resident));
 }
 
 template <int KIND, int DT, int VEC, int BLOCK>
@@ -82,6 +84,7 @@ inline Variant make_wide() {
     v.wide = true;
     v.grid_cap = 0;
     v.grid_first = false;
+    v.grid_resident = 0;
     return v;
 }
 
@@ -104,11 +107,23 @@ inline void add_wide(std::vector<Variant>& t) {
 // faster for LayerNorm than the 1024-pack one, and 2049-3072 packs (bf16
 // 18432, 24576) one of 512 threads, 10% faster for LayerNorm than the
 // 1024-thread shape.  The 1024-thread shapes (one row per workgroup) stay
-// persistent: a plain grid is 6-40% slower there.
+// persistent: a plain grid is 6-40% slower there.  LayerNorm with a bias at
+// 4097-8192 packs runs 20% faster on 16 packs per lane in 512 threads than
+// on 8 in 1024 (bf16 49152 and 65536, fp32 32768); without a bias, and for
+// RMSNorm, the 1024-thread shape is as fast or faster.
+//
+// Plain grids keep few workgroups resident per CU, so that 64-96 KB of
+// loads are in flight per CU: 3 for the shapes with 20-32 KB per workgroup,
+// 4 for the 16 KB of one row of 4 packs per lane, 2 for the 48 KB of the
+// 512-thread shape.  With as many as the registers allow they run 3-7%
+// slower (LayerNorm at bf16 5120 and 12288, RMSNorm at 12288 and 18432), with
+// fewer 5-30% slower.  The grids whose rows fit one wave with 2 or 4 packs
+// per lane (8 and 16 KB per workgroup) run best unlimited.
 template <int DT, int V>
 inline void add_masked(std::vector<Variant>& t) {
     constexpr int WIDE_NT = V > 1 ? NT_BOTH : NT_NONE;
     constexpr int WIDE_CAP = V > 1 ? GRID_FIRST : 0;
+    constexpr int R = V > 1 ? 1 : 0;   // resident limits for the 16-byte-pack grids
     add_shape<DT, V, 1, 1, 256, true, NT_NONE>(t);
     add_shape<DT, V, 1, 2, 256, true, NT_NONE>(t);
     add_shape<DT, V, 1, 4, 256, true, NT_NONE>(t);
@@ -118,12 +133,13 @@ inline void add_masked(std::vector<Variant>& t) {
     add_shape<DT, V, 1, 64, 256, true, NT_NONE>(t);
     add_shape<DT, V, 2, 64, 256, true, WIDE_NT>(t, WIDE_CAP);
     add_shape<DT, V, 4, 64, 256, true, WIDE_NT>(t, WIDE_CAP);
-    add_shape<DT, V, 8, 64, 256, true, WIDE_NT>(t, WIDE_CAP);
-    if constexpr (V > 1) add_shape<DT, V, 5, 128, 256, true, WIDE_NT>(t, WIDE_CAP);
-    add_shape<DT, V, 4, 256, 256, true, WIDE_NT>(t, WIDE_CAP);
-    add_shape<DT, V, 8, 256, 256, true, WIDE_NT>(t, WIDE_CAP);
-    if constexpr (V > 1) add_shape<DT, V, 6, 512, 512, true, WIDE_NT>(t, WIDE_CAP);
+    add_shape<DT, V, 8, 64, 256, true, WIDE_NT>(t, WIDE_CAP, 3 * R);
+    if constexpr (V > 1) add_shape<DT, V, 5, 128, 256, true, WIDE_NT>(t, WIDE_CAP, 3);
+    add_shape<DT, V, 4, 256, 256, true, WIDE_NT>(t, WIDE_CAP, 4 * R);
+    add_shape<DT, V, 8, 256, 256, true, WIDE_NT>(t, WIDE_CAP, 3 * R);
+    if constexpr (V > 1) add_shape<DT, V, 6, 512, 512, true, WIDE_NT>(t, WIDE_CAP, 2);
     add_shape<DT, V, 4, 1024, 1024, true, WIDE_NT>(t);
+    if constexpr (V > 1) add_shape<DT, V, 16, 512, 512, true, WIDE_NT, KM_LAYER_BIAS>(t);
     add_shape<DT, V, 8, 1024, 1024, true, WIDE_NT>(t);
 }
 

@@ -129,17 +129,23 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
     // Column of pack v of this thread, and whether it lies inside the row.
     auto col_of = [&](int v) { return int64_t(v * LPR + lane) * VEC; };
     auto in_row = [&](int v) { return !MASKED || col_of(v) < width; };
+    // The same column as a byte offset: a row here spans at most 8192
+    // 16-byte packs, so 32 bits hold it.
+    auto col_b = [&](int v) { return uint32_t((v * LPR + lane) * VEC * Elem<DT>::bytes); };
+    const char* const wb = static_cast<const char*>(a.w);
+    const char* const bb = static_cast<const char*>(a.b);
+    const char* const w2b = static_cast<const char*>(a.w2);
 
     R wv[VPT];
     R bv[BIAS ? VPT : 1];
     R wv2[DUAL ? VPT : 1];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
-        wv[v] = in_row(v) ? load_raw<DT, VEC, false>(a.w, col_of(v)) : raw_zero<DT, VEC>();
+        wv[v] = in_row(v) ? load_at<DT, VEC, false>(wb, col_b(v)) : raw_zero<DT, VEC>();
         if constexpr (BIAS)
-            bv[v] = in_row(v) ? load_raw<DT, VEC, false>(a.b, col_of(v)) : raw_zero<DT, VEC>();
+            bv[v] = in_row(v) ? load_at<DT, VEC, false>(bb, col_b(v)) : raw_zero<DT, VEC>();
         if constexpr (DUAL)
-            wv2[v] = in_row(v) ? load_raw<DT, VEC, false>(a.w2, col_of(v)) : raw_zero<DT, VEC>();
+            wv2[v] = in_row(v) ? load_at<DT, VEC, false>(w2b, col_b(v)) : raw_zero<DT, VEC>();
     }
 
     // Where block-row `base` of this thread's row group lives.  Row groups
@@ -148,10 +154,9 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
     // before this row's reductions measured slower on every bench shape.)
     struct Loc {
         bool valid, second;   // second: uniform over the workgroup
-        const void* xp;
-        void* yp;
-        RowOff off;
-        int64_t goff;
+        const char* xr;       // first byte of the row, input and output
+        char* yr;
+        const char* gr;       // and of its gate row
     };
     auto locate = [&](int64_t unit) {
         Loc L;
@@ -160,24 +165,22 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
         const int64_t last = (DUAL ? (L.second ? a.rows - a.rows1 : a.rows1) : a.rows) - 1;
         L.valid = base + group <= last;
         const int64_t r = L.valid ? base + group : last;   // row of this tensor
-        L.xp = L.second ? a.x2 : a.x;
-        L.yp = L.second ? a.y2 : a.y;
-        L.off = L.second ? row_offsets(r, a.x2h, a.x2div, a.x2s, a.y2s, width)
-                         : row_offsets(r, a.xh, a.xdiv, a.xs, a.ys, width);
-        L.goff = GATED ? r * a.gs : 0;
+        const RowOff off = L.second ? row_offsets(r, a.x2h, a.x2div, a.x2s, a.y2s, width)
+                                    : row_offsets(r, a.xh, a.xdiv, a.xs, a.ys, width);
+        L.xr = static_cast<const char*>(L.second ? a.x2 : a.x) + off.x * Elem<DT>::bytes;
+        L.yr = static_cast<char*>(L.second ? a.y2 : a.y) + off.y * Elem<DT>::bytes;
+        L.gr = GATED ? static_cast<const char*>(a.g) + r * a.gs * Elem<DT>::bytes : nullptr;
         return L;
     };
     auto load_row = [&](const Loc& L, R* dst) {
 #pragma unroll
         for (int v = 0; v < VPT; ++v)
-            dst[v] = in_row(v) ? load_raw<DT, VEC, NT_LD>(L.xp, L.off.x + col_of(v))
-                               : raw_zero<DT, VEC>();
+            dst[v] = in_row(v) ? load_at<DT, VEC, NT_LD>(L.xr, col_b(v)) : raw_zero<DT, VEC>();
     };
     auto load_gate = [&](const Loc& L, R* dst) {
 #pragma unroll
         for (int v = 0; v < VPT; ++v)
-            dst[v] = in_row(v) ? load_raw<DT, VEC, NT_LD>(a.g, L.goff + col_of(v))
-                               : raw_zero<DT, VEC>();
+            dst[v] = in_row(v) ? load_at<DT, VEC, NT_LD>(L.gr, col_b(v)) : raw_zero<DT, VEC>();
     };
 
     int parity = 0;
@@ -236,8 +239,7 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
                         for (int i = 0; i < VEC; ++i) o[i] *= silu(elem<DT, VEC>(gv[v], i));
                     }
                     if (in_row(v))
-                        store_raw<DT, VEC, NT_ST>(cur.yp, cur.off.y + col_of(v),
-                                                  make_raw<DT, VEC>(o));
+                        store_at<DT, VEC, NT_ST>(cur.yr, col_b(v), make_raw<DT, VEC>(o));
                 });
             }
         } else {
@@ -278,8 +280,7 @@ __global__ __launch_bounds__(BLOCK) void norm_rows(NormArgs a) {
                         o[i] = __builtin_fmaf(d * scale, elem<DT, VEC>(wv[v], i), bias);
                     }
                     if (in_row(v))
-                        store_raw<DT, VEC, NT_ST>(cur.yp, cur.off.y + col_of(v),
-                                                  make_raw<DT, VEC>(o));
+                        store_at<DT, VEC, NT_ST>(cur.yr, col_b(v), make_raw<DT, VEC>(o));
                 });
             }
         }

@@ -32,6 +32,8 @@ struct Variant {
     bool wide;          // non-resident multi-pass kernel
     int grid_cap;       // persistent grid: workgroups per CU (0 = as many as fit)
     bool grid_first;    // default launch is one workgroup per block-row, not persistent
+    int grid_resident;  // plain grid: at most this many workgroups resident per CU (0 = as
+                        // many as fit), held there by a reservation of dynamic LDS
     int64_t capacity() const { return wide ? INT64_MAX : int64_t(lpr) * vpt * vec; }
     int rows_per_block() const { return wide ? 1 : block / lpr; }
 };
