@@ -187,10 +187,12 @@ def test_launch_policy_and_per_kind_order():
             assert len(set(names)) == n, names
             assert sum(".vpt4.lpr256.blk256.exact.nt.persistent2" in x for x in names) == 1
             assert sum(".vpt4.lpr256.blk256.exact.ntld.persistent2" in x for x in names) == 1
-    # head vectors of 8 and 32 packs: exact shapes with non-temporal access
-    assert trn.describe(trn.OP_DUAL, BF16, 64) == "dual.bf16.vec8.vpt1.lpr8.blk256.exact.nt.persistent"
-    assert trn.describe(trn.OP_DUAL, BF16, 256) == "dual.bf16.vec8.vpt1.lpr32.blk256.exact.nt.persistent"
-    assert trn.describe(trn.OP_DUAL, F32, 128) == "dual.f32.vec4.vpt1.lpr32.blk256.exact.nt.persistent"
+    # head vectors of 8-32 packs: exact shapes with non-temporal access on a plain grid
+    assert trn.describe(trn.OP_DUAL, BF16, 64) == "dual.bf16.vec8.vpt1.lpr8.blk256.exact.nt.grid"
+    assert trn.describe(trn.OP_DUAL, BF16, 128) == "dual.bf16.vec8.vpt2.lpr8.blk256.exact.nt.grid"
+    assert trn.describe(trn.OP_DUAL, BF16, 256) == "dual.bf16.vec8.vpt1.lpr32.blk256.exact.nt.grid"
+    assert trn.describe(trn.OP_DUAL, F32, 128) == "dual.f32.vec4.vpt1.lpr32.blk256.exact.nt.grid"
+    assert trn.describe(trn.OP_DUAL, BF16, 128, variant=1) == "dual.bf16.vec8.vpt2.lpr8.blk256.exact.nt.persistent"
     # 4-8 packs per lane at 128, 256 and 2048 packs
     assert ".vpt4.lpr32." in trn.describe(trn.OP_LAYER, BF16, 1024)
     assert ".vpt4.lpr64." in trn.describe(trn.OP_RMS, F32, 1024)
@@ -334,7 +336,7 @@ def test_rms_swiglu_validation(lib):
     assert st(A, 16, A + 16, 16, B, C, 8, 4, 8, 1e-6) == 6    # x and g interleaved in one buffer
     assert lib.fnorm_last_error().startswith(b"fnorm_rms_swiglu_strided: ")
     assert trn.variant_count(trn.OP_RMS_SWIGLU, BF16, 128) >= 2
-    assert trn.describe(trn.OP_RMS_SWIGLU, BF16, 128).startswith("rmsgate.bf16.vec8.vpt1.lpr16")
+    assert trn.describe(trn.OP_RMS_SWIGLU, BF16, 128).startswith("rmsgate.bf16.vec8.vpt2.lpr8")
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")

@@ -166,18 +166,24 @@ inline void add_masked(std::vector<Variant>& t) {
 template <int DT>
 inline void register_dtype(std::vector<Variant>& t) {
     constexpr int V = 16 / Elem<DT>::bytes;
+    // Head-sized rows (8-32 packs) run on a plain grid: a persistent grid
+    // caps the dual near 5.2 TB/s however many tokens there are, while the
+    // plain grid reaches the copy kernel's rate from 8192 tokens on (bf16
+    // head_dim 128, 32 query + 8 key heads: 32768 tokens 106 against 129 us,
+    // 4096 tokens 17.8 against 18.2 us).
     // 8 packs (bf16 64 / f32 32): one 8-lane group per row (dual at head_dim
     // 64: 8-12% faster than the masked 8-lane shape with ordinary access)
-    FNORM_EXACT(1, 8, 256, NT_BOTH, 0)
+    FNORM_EXACT(1, 8, 256, NT_BOTH, GRID_FIRST)
     FNORM_EXACT(1, 8, 256, NT_NONE, 0)
-    // 16 packs (bf16 128 / f32 64): one 16-lane group per row
+    // 16 packs (bf16 128 / f32 64): an 8-lane group per row, 2 packs per
+    // lane (32 rows per workgroup)
+    FNORM_EXACT(2, 8, 256, NT_BOTH, GRID_FIRST)
     FNORM_EXACT(1, 16, 256, NT_BOTH, 0)
     FNORM_EXACT(1, 16, 256, NT_LOAD, 0)
     FNORM_EXACT(1, 16, 256, NT_NONE, 0)
-    FNORM_EXACT(2, 8, 256, NT_BOTH, 0)
     // 32 packs (bf16 256 / f32 128; dual at those head sizes: non-temporal
     // stores 4-5% faster)
-    FNORM_EXACT(1, 32, 256, NT_BOTH, 0)
+    FNORM_EXACT(1, 32, 256, NT_BOTH, GRID_FIRST)
     FNORM_EXACT(1, 32, 256, NT_LOAD, 0)
     FNORM_EXACT(2, 16, 256, NT_NONE, 0)
     FNORM_EXACT(1, 32, 256, NT_NONE, 0)
