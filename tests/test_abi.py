@@ -249,13 +249,15 @@ def test_rope_validation(lib):
     assert call(qh=-2) == 2
     assert call(eps=-1.0) == 3
     assert call(dt=5) == 4
+    assert call(hd=8192, dims=8192) == 6    # more pairs than the frequency tables carry
     assert call(tokens=0) == 0
     assert lib.fnorm_last_error() == b""
     # head shapes the kernel cannot serve are refused, not run
     assert trn.rope_variant_count(BF16, 1024, 128, False) == 0
     assert trn.rope_variant_count(BF16, 128, 128, False) >= 2
     assert trn.rope_variant_count(BF16, 128, 128, True) >= 2
-    assert "lpr16" in trn.describe_rope(BF16, 128, 128, False)
+    assert trn.describe_rope(BF16, 128, 128, False) == "ropesplit.bf16.vec8.vpt2.lpr8.blk256.exact.nt.grid"
+    assert trn.describe_rope(BF16, 64, 64, False) == "ropesplit.bf16.vec8.vpt1.lpr8.blk256.exact.nt.persistent"
     assert trn.rope_variant_count(BF16, 128, 127, False) == 0
 
 

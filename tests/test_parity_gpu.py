@@ -470,6 +470,10 @@ ROPE_CASES = [  # (dtype, tokens, q_heads, k_heads, head_dim, dims, traditional,
     # long contexts: the angle is formed in fp64 and reduced in turns
     (torch.float32, 24, 4, 2, 128, 128, False, 10000.0, 1.0, 1 << 24, False),
     (torch.bfloat16, 24, 8, 2, 128, 128, True, 1000000.0, 1.0, 1000000, False),
+    # more than 256 frequency pairs: the host table's later pairs come from
+    # its step factors; and a caller's table of 512 pairs
+    (torch.bfloat16, 9, 2, 1, 2048, 2048, False, 10000.0, 1.0, 777, False),
+    (torch.float32, 7, 2, 1, 1024, 1024, False, 10000.0, 1.0, 5, True),
 ]
 
 

@@ -7,6 +7,7 @@
 // (operation name + description, structural checks before any work).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -134,11 +135,45 @@ bool rope_ok(const Variant& v, int64_t dims) {
     return dp % v.lpr == 0;
 }
 
-// LDS bytes of a fused RoPE launch: inverse frequencies (fp64) plus one
-// (cos, sin) fp32 table per row slot.
+// LDS bytes of a fused RoPE launch: one (cos, sin) fp32 table per row slot.
 int64_t rope_lds_bytes(const Variant& v, int64_t dims) {
     const int64_t half = dims / 2;
-    return half * 8 + int64_t(v.rows_per_block()) * half * 8;
+    return int64_t(v.rows_per_block()) * half * 8;
+}
+
+// The inverse-frequency tables of the kernel arguments for (base, dims), in
+// turns per position: (1 / 2 pi) * exp2(-2i/dims * log2(base)) for the first
+// kRopeTable pairs, and the factors exp2(-2 j kRopeTable / dims * log2(base))
+// that carry them to the later pairs, fp64.  The last few tables are kept
+// per thread, so a decode-size call copies one.
+struct RopeTable {
+    float base = 0.0f;
+    int64_t dims = -1;
+    double invf[RopeArgs::kRopeTable];
+    double invf_step[RopeArgs::kRopeSteps];
+};
+
+const RopeTable& rope_table(float base, int64_t dims) {
+    constexpr int kSlots = 4;
+    thread_local RopeTable cache[kSlots];
+    thread_local int next = 0;
+    for (const RopeTable& e : cache)
+        if (e.dims == dims && e.base == base) return e;
+    RopeTable& e = cache[next];
+    next = (next + 1) % kSlots;
+    constexpr double kInvTwoPi = 0.15915494309189533577;
+    const double lb = std::log2(static_cast<double>(base));
+    const int64_t n = std::min<int64_t>(dims / 2, RopeArgs::kRopeTable);
+    for (int64_t i = 0; i < RopeArgs::kRopeTable; ++i)
+        e.invf[i] = i < n ? kInvTwoPi * std::exp2(-2.0 * static_cast<double>(i) /
+                                                  static_cast<double>(dims) * lb)
+                          : 0.0;
+    for (int j = 0; j < RopeArgs::kRopeSteps; ++j)
+        e.invf_step[j] = std::exp2(-2.0 * static_cast<double>(j * RopeArgs::kRopeTable) /
+                                   static_cast<double>(dims) * lb);
+    e.base = base;
+    e.dims = dims;
+    return e;
 }
 
 constexpr int64_t kMaxLds = 64 * 1024;
@@ -563,6 +598,9 @@ int rope_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
     if (rope_dims < 2 || rope_dims % 2 != 0 || rope_dims > head_dim)
         return fail(FNORM_ERR_SHAPE, op, "rope_dims=%lld must be even and in [2, head_dim=%lld]",
                     (long long)rope_dims, (long long)head_dim);
+    if (rope_dims / 2 > int64_t(RopeArgs::kRopeTable) * RopeArgs::kRopeSteps)
+        return fail(FNORM_ERR_UNSUPPORTED, op, "rope_dims=%lld above %lld", (long long)rope_dims,
+                    2LL * RopeArgs::kRopeTable * RopeArgs::kRopeSteps);
     if (!std::isfinite(scale) || (!freqs && (!std::isfinite(base) || base <= 0.0f)))
         return fail(FNORM_ERR_SHAPE, op, "base must be finite and > 0, scale finite");
     if (offset < 0 || tokens < 0 || offset > (int64_t(1) << 52) - tokens)
@@ -583,7 +621,7 @@ int rope_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
                     "no fused kernel for head_dim %lld, rope_dims %lld (variant %d)",
                     (long long)head_dim, (long long)rope_dims, variant);
     const Variant* v = list[variant / 2];
-    const bool persistent = variant % 2 == 0;
+    const bool persistent = (variant % 2 == 0) != v->grid_first;
     const void* qw_eff = q_rows > 0 ? qw : kw;
     const void* kw_eff = k_rows > 0 ? kw : qw;
     RopeArgs ra{NormArgs{q, qw_eff, nullptr, qy, k, kw_eff, ky, q_rows + k_rows, q_rows,
@@ -592,6 +630,11 @@ int rope_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
                 q_heads > 0 ? q_heads : 1, k_heads > 0 ? k_heads : 1, rope_dims, offset, base,
                 scale, freqs, FastDiv{}, FastDiv{}, 0u};
     ra.n.inv_width = 1.0f / static_cast<float>(head_dim);
+    if (!freqs) {
+        const RopeTable& tab = rope_table(base, rope_dims);
+        std::memcpy(ra.invf, tab.invf, sizeof(ra.invf));
+        std::memcpy(ra.invf_step, tab.invf_step, sizeof(ra.invf_step));
+    }
     // the kernel divides by the head counts only while rows < 2^31
     if (ra.n.rows <= 0x7fffffff) {
         ra.qdiv = make_fast_div(uint32_t(ra.q_heads));
@@ -783,7 +826,7 @@ int fnorm_describe_rope(int dtype, int64_t head_dim, int64_t rope_dims, int trad
                     rope_dims, list);
     Choice c;
     c.v = list[variant / 2];
-    c.persistent = variant % 2 == 0;
+    c.persistent = (variant % 2 == 0) != c.v->grid_first;
     describe_choice(c, buf, size_t(len));
     return ok();
 }

@@ -7,7 +7,7 @@ namespace fnorm {
 namespace {
 
 template <int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, int NT, bool TRAD>
-Variant make_rope() {
+Variant make_rope(bool grid_first) {
     Variant v{};
     v.fn = reinterpret_cast<const void*>(&dual_rope_rows<DT, VEC, VPT, LPR, BLOCK, MASKED, NT, TRAD>);
     v.kind = TRAD ? K_ROPE_TRAD : K_ROPE_SPLIT;
@@ -20,13 +20,16 @@ Variant make_rope() {
     v.nt = NT;
     v.wide = false;
     v.grid_cap = 0;
+    v.grid_first = grid_first;
     return v;
 }
 
+// grid_first: the default launch is one workgroup per block of rows, the
+// persistent grid the other variant.
 template <int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, int NT>
-void add_rope(std::vector<Variant>& t) {
-    t.push_back(make_rope<DT, VEC, VPT, LPR, BLOCK, MASKED, NT, false>());
-    t.push_back(make_rope<DT, VEC, VPT, LPR, BLOCK, MASKED, NT, true>());
+void add_rope(std::vector<Variant>& t, bool grid_first = false) {
+    t.push_back(make_rope<DT, VEC, VPT, LPR, BLOCK, MASKED, NT, false>(grid_first));
+    t.push_back(make_rope<DT, VEC, VPT, LPR, BLOCK, MASKED, NT, true>(grid_first));
 }
 
 template <int DT, int V>
@@ -47,11 +50,18 @@ template <int DT>
 void register_rope_dtype(std::vector<Variant>& t) {
     constexpr int V = 16 / Elem<DT>::bytes;
     // exact head-vector shapes (bf16 head_dim 64/128/256/512, f32 32/64/128/256)
-    // (preference order measured on MI355X for head_dim 128 bf16, at 4096
-    // tokens and at one decode token: 256-thread workgroups with
-    // non-temporal loads and stores first; the cache policy changes the
-    // full-size time by under 5%)
+    // (preference order measured on MI355X, cold buffers, 32 query + 8 key
+    // heads: 256-thread workgroups with non-temporal loads and stores; the
+    // cache policy changes the full-size time by under 5%).  Rows of 16 and
+    // 32 packs hold 2 packs per lane, so a split-half partner is in the same
+    // thread, on a plain grid: at head_dim 128 (bf16) 19.6 against 19.9 us
+    // for one pack per lane on a persistent grid at 4096 tokens, 58.7
+    // against 62.6 at 16384, 110.8 against 124.2 at 32768; at head_dim 256
+    // 149.5 against 186.3 at 16384.  Rows of 8 packs keep one pack per lane
+    // on a persistent grid (34.7 against 37.2 us at 16384 tokens).
     add_rope<DT, V, 1, 8, 256, false, NT_BOTH>(t);
+    add_rope<DT, V, 2, 8, 256, false, NT_BOTH>(t, true);
+    add_rope<DT, V, 2, 16, 256, false, NT_BOTH>(t, true);
     add_rope<DT, V, 1, 16, 256, false, NT_BOTH>(t);
     add_rope<DT, V, 1, 16, 512, false, NT_BOTH>(t);
     add_rope<DT, V, 1, 16, 1024, false, NT_BOTH>(t);

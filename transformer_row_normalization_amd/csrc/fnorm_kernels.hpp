@@ -417,8 +417,10 @@ namespace fnorm {
 // are consecutive rows.  Each wavefront evaluates the (cos, sin) table once
 // per token among its rows (the first slot of each token, found with one
 // ballot) into its own LDS region, and every row of that token reads it;
-// the table is private to the wavefront, so no workgroup barrier is needed
-// in the row loop.  The angle in turns, theta / (2 pi), is formed
+// the table is private to the wavefront, and the inverse frequencies come
+// in the kernel arguments, so the kernel has no workgroup barrier and no
+// per-workgroup set-up beyond its weight loads.  The angle in turns,
+// theta / (2 pi), is formed
 // in fp64 and reduced exactly to its fractional part f in [-1/2, 1/2]; sin
 // and cos of 2 pi f then come from the hardware v_sin_f32 / v_cos_f32 (which
 // take turns), so large positions keep fp32-level accuracy at the cost of a
@@ -441,6 +443,16 @@ struct RopeArgs {
     const float* freqs;  // dims/2 inverse frequencies, or null
     FastDiv qdiv, kdiv;  // division by q_heads / k_heads (rows < 2^31)
     uint32_t q_blocks;   // workgroups [0, q_blocks) serve the queries, the rest the keys
+    // Inverse frequencies in turns per position, base^(-2i/dims) / (2 pi),
+    // computed by the host in fp64 (unused with freqs): pair i's is
+    // invf[i % kRopeTable] * invf_step[i / kRopeTable], where invf_step[j] =
+    // base^(-2 j kRopeTable / dims), so dims/2 may reach kRopeTable *
+    // kRopeSteps.  Kernel arguments, so a workgroup starts without a
+    // prologue: its lanes read the entries they need straight from here.
+    static constexpr int kRopeTable = 256;
+    static constexpr int kRopeSteps = 8;
+    double invf[kRopeTable];
+    double invf_step[kRopeSteps];
 };
 
 template <int DT, int VEC, int VPT, int LPR, int BLOCK, bool MASKED, int NT, bool TRAD>
@@ -450,7 +462,7 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
     constexpr int RPB = BLOCK / LPR;
     constexpr bool NT_LD = (NT & NT_LOAD) != 0;
     constexpr bool NT_ST = (NT & NT_STORE) != 0;
-    extern __shared__ double rope_smem[];   // inv_freq[half], then (cos, sin)[RPB][half]
+    extern __shared__ double rope_smem[];   // (cos, sin)[RPB][half]
 
     const NormArgs& a = ra.n;
     const int tid = threadIdx.x;
@@ -477,22 +489,18 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
     const int64_t ys = second ? a.y2s : a.ys;
     const int64_t den = second ? ra.k_heads : ra.q_heads;
     const FastDiv hdiv = second ? ra.kdiv : ra.qdiv;
-    double* invf = rope_smem;
-    float2* cs = reinterpret_cast<float2*>(rope_smem + half);
+    float2* cs = reinterpret_cast<float2*>(rope_smem);
 
-    // inverse frequencies in turns per position: inv_freq_i / (2 pi), fp64
-    // (base^(-2i/dims) as exp2(-2i/dims * log2(base)) in fp64: half the
-    // work of pow, relative error ~1e-15, which moves an angle by under
-    // 1e-9 rad at a million positions)
+    // Inverse frequency of pair i in turns per position (inv_freq_i / (2 pi),
+    // fp64): the caller's frequencies, else the host's table (relative error
+    // ~1e-15 past its first kRopeTable pairs, which moves an angle by under
+    // 1e-9 rad at a million positions).
     constexpr double kInvTwoPi = 0.15915494309189533577;
-    if (tid < half) {
-        const double lb = ra.freqs ? 0.0 : log2(static_cast<double>(ra.base));
-        for (int64_t i = tid; i < half; i += BLOCK)
-            invf[i] = kInvTwoPi *
-                      (ra.freqs ? static_cast<double>(ra.freqs[i])
-                                : exp2(-2.0 * static_cast<double>(i) /
-                                       static_cast<double>(ra.dims) * lb));
-    }
+    auto inv_turns = [&](int i) -> double {
+        if (ra.freqs) return kInvTwoPi * static_cast<double>(ra.freqs[i]);
+        if (i < RopeArgs::kRopeTable) return ra.invf[i];
+        return ra.invf[i % RopeArgs::kRopeTable] * ra.invf_step[i / RopeArgs::kRopeTable];
+    };
 
     auto col_of = [&](int v) { return int64_t(v * LPR + lane) * VEC; };
     auto in_row = [&](int v) { return !MASKED || col_of(v) < width; };
@@ -506,7 +514,6 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
         wv[v] = in_row(v) ? load_raw<DT, VEC, false>(wp, col_of(v)) : raw_zero<DT, VEC>();
-    __syncthreads();   // inverse frequencies ready; no workgroup barrier after this
 
     const bool small = a.rows <= 0x7fffffff;
     for (int64_t base = xcd_major(seg_block, seg_grid, (seg_rows + RPB - 1) / RPB) * RPB;
@@ -551,7 +558,7 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
                 // theta / (2 pi) in fp64, reduced to a fraction of a turn
                 // exactly (t - rint(t)); the hardware sine and cosine take
                 // their argument in turns (v_sin_f32 / v_cos_f32)
-                const double t = pg * invf[i];
+                const double t = pg * inv_turns(i);
                 const float f = static_cast<float>(t - __builtin_rint(t));
                 wtab[g * ihalf + i] =
                     make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
