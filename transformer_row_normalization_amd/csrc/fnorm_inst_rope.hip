@@ -56,11 +56,21 @@ void register_rope_dtype(std::vector<Variant>& t) {
     // 32 packs hold 2 packs per lane, so a split-half partner is in the same
     // thread, on a plain grid: at head_dim 128 (bf16) 19.6 against 19.9 us
     // for one pack per lane on a persistent grid at 4096 tokens, 58.7
-    // against 62.6 at 16384, 110.8 against 124.2 at 32768; at head_dim 256
-    // 149.5 against 186.3 at 16384.  Rows of 8 packs keep one pack per lane
-    // on a persistent grid (34.7 against 37.2 us at 16384 tokens).
+    // against 62.6 at 16384, 110.8 against 124.2 at 32768.  With 2-byte
+    // elements, rows of 32 and 64 packs take 4 packs per lane, so that a
+    // wavefront holds 8 and 4 rows and builds fewer angle tables per row:
+    // bf16 head_dim 256 at 16384 tokens 126.8 us against 151.4 with 2 packs
+    // per lane and 186.0 with one; head_dim 512 at 4096 tokens 94.2 against
+    // 110.7 with one.  fp32 head_dim 128 (32 packs of 4) is 3% faster with 2
+    // packs per lane, and 4 packs in 4 lanes at bf16 head_dim 128 were
+    // slower (22.6 us).  Rows of 8 packs keep one pack per lane on a
+    // persistent grid (34.7 against 37.2 us at 16384 tokens).
     add_rope<DT, V, 1, 8, 256, false, NT_BOTH>(t);
     add_rope<DT, V, 2, 8, 256, false, NT_BOTH>(t, true);
+    if constexpr (Elem<DT>::bytes == 2) {
+        add_rope<DT, V, 4, 8, 256, false, NT_BOTH>(t, true);
+        add_rope<DT, V, 4, 16, 256, false, NT_BOTH>(t, true);
+    }
     add_rope<DT, V, 2, 16, 256, false, NT_BOTH>(t, true);
     add_rope<DT, V, 1, 16, 256, false, NT_BOTH>(t);
     add_rope<DT, V, 1, 16, 512, false, NT_BOTH>(t);
