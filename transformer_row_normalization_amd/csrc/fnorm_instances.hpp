@@ -166,7 +166,7 @@ inline void add_masked(std::vector<Variant>& t) {
 template <int DT>
 inline void register_dtype(std::vector<Variant>& t) {
     constexpr int V = 16 / Elem<DT>::bytes;
-    // Head-sized rows (8-32 packs) run on a plain grid: a persistent grid
+    // Head-sized rows (8-64 packs) run on a plain grid: a persistent grid
     // caps the dual near 5.2 TB/s however many tokens there are, while the
     // plain grid reaches the copy kernel's rate from 8192 tokens on (bf16
     // head_dim 128, 32 query + 8 key heads: 32768 tokens 106 against 129 us,
@@ -187,8 +187,9 @@ inline void register_dtype(std::vector<Variant>& t) {
     FNORM_EXACT(1, 32, 256, NT_LOAD, 0)
     FNORM_EXACT(2, 16, 256, NT_NONE, 0)
     FNORM_EXACT(1, 32, 256, NT_NONE, 0)
-    // 64 packs
-    FNORM_EXACT(1, 64, 256, NT_LOAD, 0)
+    // 64 packs (bf16 512 / f32 256): a plain grid (dual at head_dim 512,
+    // 16384 tokens: 218 against 264 us persistent)
+    FNORM_EXACT(1, 64, 256, NT_LOAD, GRID_FIRST)
     FNORM_EXACT(1, 64, 256, NT_NONE, 0)
     // 96 packs (bf16 768)
     FNORM_EXACT(3, 32, 256, NT_BOTH, GRID_FIRST)
