@@ -159,6 +159,10 @@ def test_launch_policy_and_per_kind_order():
     assert trn.describe(trn.OP_RMS, BF16, 5120).startswith("rms.bf16.vec8.vpt5.lpr128.")
     # the shortest masked rows run without a limit
     assert trn.describe(trn.OP_RMS, BF16, 640).endswith(".masked.nt.grid")
+    # 33-64 packs: 2 packs per lane on a plain grid; fewer: one pack, persistent
+    for w in (264, 320, 504):
+        assert trn.describe(trn.OP_LAYER, BF16, w) == "layer.bf16.vec8.vpt2.lpr32.blk256.masked.nt.grid"
+    assert trn.describe(trn.OP_RMS, BF16, 200) == "rms.bf16.vec8.vpt1.lpr32.blk256.masked.persistent"
     for w in (18432, 24576):
         d = trn.describe(trn.OP_LAYER, BF16, w)
         assert d.startswith("layer.bf16.vec8.vpt6.lpr512.blk512.masked.nt.") and d.endswith(".grid2"), d
