@@ -128,7 +128,9 @@ inline void add_masked(std::vector<Variant>& t) {
     add_shape<DT, V, 1, 2, 256, true, NT_NONE>(t);
     add_shape<DT, V, 1, 4, 256, true, NT_NONE>(t);
     add_shape<DT, V, 1, 8, 256, true, NT_NONE>(t);
-    add_shape<DT, V, 1, 16, 256, true, NT_NONE>(t);
+    // 9-16 packs (e.g. bf16 head_dim 96): non-temporal loads and stores,
+    // 4-5% faster than ordinary ones (bf16 96 and 120)
+    add_shape<DT, V, 1, 16, 256, true, (V > 1 ? NT_BOTH : NT_NONE)>(t);
     add_shape<DT, V, 1, 32, 256, true, NT_NONE>(t);
     // 33-64 packs: 2 packs per lane on a plain grid, 4-14% faster than one
     // pack per lane on a persistent grid (bf16 264-504, fp32 132-252).  The
