@@ -475,6 +475,10 @@ ROPE_CASES = [  # (dtype, tokens, q_heads, k_heads, head_dim, dims, traditional,
     # its step factors; and a caller's table of 512 pairs
     (torch.bfloat16, 9, 2, 1, 2048, 2048, False, 10000.0, 1.0, 777, False),
     (torch.float32, 7, 2, 1, 1024, 1024, False, 10000.0, 1.0, 5, True),
+    # partial rotation on shapes with several packs per lane (the pairing is
+    # then chosen at run time): half the features of head_dim 256 and 512
+    (torch.bfloat16, 29, 6, 2, 256, 128, False, 10000.0, 1.0, 31, False),
+    (torch.bfloat16, 13, 4, 1, 512, 256, False, 500000.0, 1.0, 8, False),
 ]
 
 

@@ -662,23 +662,42 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
                                            : o[0][i] * t[i].x + q[i] * t[i].y;
                 }
             } else {
-                // the partner pack is in this thread, dp / LPR packs away
-                // (the host launches VPT > 1 only when dp % LPR == 0)
+                // the partner pack is in this thread, dv = dp / LPR packs
+                // away (the host launches VPT > 1 only when dp % LPR == 0).
+                // Pack v is rotated when v < 2 dv and pairs with pack v + dv
+                // (v < dv) or v - dv: conditions on v alone, uniform.
                 const int dv = int(dp / LPR);
-#pragma unroll
-                for (int v = 0; v < VPT; ++v) {
-                    const int64_t p = int64_t(v) * LPR + lane;
-                    if (p < 2 * dp) {
-                        const bool first = p < dp;
-                        const int vp = first ? v + dv : v - dv;
+                if (2 * dv == VPT) {
+                    // every feature rotates: the pairing is known at compile time
+                    static_for<VPT>([&](auto vi) {
+                        constexpr int v = decltype(vi)::value;
+                        constexpr bool first = v < VPT / 2;
+                        constexpr int vp = first ? v + VPT / 2 : v - VPT / 2;
+                        constexpr int tv = first ? v : vp;
 #pragma unroll
                         for (int i = 0; i < VEC; ++i) {
-                            float q = 0.0f;
+                            const float2 t = tab[(tv * LPR + lane) * VEC + i];
+                            out[v][i] = first ? o[v][i] * t.x - o[vp][i] * t.y
+                                              : o[v][i] * t.x + o[vp][i] * t.y;
+                        }
+                    });
+                } else {
 #pragma unroll
-                            for (int u = 0; u < VPT; ++u)
-                                if (u == vp) q = o[u][i];
-                            const float2 t = tab[(first ? p : p - dp) * VEC + i];
-                            out[v][i] = first ? o[v][i] * t.x - q * t.y : o[v][i] * t.x + q * t.y;
+                    for (int v = 0; v < VPT; ++v) {
+                        if (v < 2 * dv) {
+                            const bool first = v < dv;
+                            const int vp = first ? v + dv : v - dv;
+                            const int tv = first ? v : vp;
+#pragma unroll
+                            for (int i = 0; i < VEC; ++i) {
+                                float q = 0.0f;
+#pragma unroll
+                                for (int u = 0; u < VPT; ++u)
+                                    if (u == vp) q = o[u][i];
+                                const float2 t = tab[(tv * LPR + lane) * VEC + i];
+                                out[v][i] = first ? o[v][i] * t.x - q * t.y
+                                                  : o[v][i] * t.x + q * t.y;
+                            }
                         }
                     }
                 }
