@@ -141,7 +141,9 @@ int fnorm_dual_head_rms(const void* q, const void* k, const void* qw, const void
  * rope_dims must be even, 2 <= rope_dims <= head_dim; base finite and > 0
  * (unless freqs), scale finite, offset >= 0; else FNORM_ERR_SHAPE.
  * Head shapes whose pair partners the kernel cannot reach (some partial
- * rope_dims on wide heads) return FNORM_ERR_UNSUPPORTED.
+ * rope_dims on wide heads), and rope_dims above 4096 (the host's fp64
+ * frequency tables, passed in the kernel arguments, cover 2048 pairs),
+ * return FNORM_ERR_UNSUPPORTED.
  */
 int fnorm_dual_head_rms_rope(const void* q, const void* k, const void* qw, const void* kw,
                              void* qy, void* ky, int64_t tokens, int64_t q_heads,
