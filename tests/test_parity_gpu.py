@@ -303,6 +303,29 @@ def test_deterministic():
     assert torch.equal(r0.view(torch.int16), r1.view(torch.int16))
 
 
+@pytest.mark.parametrize("op,dtype,width", [("rms", torch.bfloat16, 128), ("layer", torch.bfloat16, 360),
+                                             ("layer", torch.bfloat16, 5120), ("rms", torch.bfloat16, 12288),
+                                             ("layer", torch.float32, 3000), ("layer", torch.bfloat16, 4096),
+                                             ("rms", torch.bfloat16, 18432)])
+def test_launch_forms_bitwise_equal(op, dtype, width):
+    """The two launch forms of one kernel (variants 2i and 2i + 1: a plain grid,
+    with or without a resident limit, and a persistent grid) compute every row
+    with the same code, so their outputs are bitwise equal; rows chosen so the
+    persistent grid loops several times and the plain grid is far larger than
+    what fits at once."""
+    rows = max(64, (48 << 20) // (width * torch.tensor([], dtype=dtype).element_size()))
+    t = inputs.random_rows(op, rows, width, dtype, seed=width + 1, mean=0.5, std=1.5)
+    code = dcode(dtype)
+    opc = trn.OP_RMS if op == "rms" else trn.OP_LAYER
+    say(f"[forms] {op} {dtype} rows={rows} width={width} {trn.describe(opc, code, width, variant=0)}")
+    y0 = run_gpu(op, t, 1e-5, variant=0)
+    y1 = run_gpu(op, t, 1e-5, variant=1)
+    assert trn.describe(opc, code, width, variant=0).rsplit(".", 1)[0] == \
+        trn.describe(opc, code, width, variant=1).rsplit(".", 1)[0]
+    assert torch.equal(y0.view(torch.int16 if dtype != torch.float32 else torch.int32),
+                       y1.view(torch.int16 if dtype != torch.float32 else torch.int32))
+
+
 def test_special_rows(o):
     """Zero rows, constant rows, NaN and infinity propagate as the oracle says."""
     for dtype in (torch.float32, torch.bfloat16, torch.float16):
