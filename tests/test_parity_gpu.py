@@ -326,6 +326,23 @@ def test_launch_forms_bitwise_equal(op, dtype, width):
                        y1.view(torch.int16 if dtype != torch.float32 else torch.int32))
 
 
+@pytest.mark.parametrize("hd,trad", [(128, False), (128, True), (256, False), (64, False)])
+def test_rope_launch_forms_bitwise_equal(hd, trad):
+    """The fused RoPE launch's two forms (plain and persistent grid) run the
+    same kernel: bitwise-equal outputs over 2048 tokens of 32 + 8 heads."""
+    g = torch.Generator(device="cpu").manual_seed(hd + int(trad))
+    q = torch.randn(2048, 32, hd, generator=g).to(torch.bfloat16).to(DEV)
+    k = torch.randn(2048, 8, hd, generator=g).to(torch.bfloat16).to(DEV)
+    qw = (1 + 0.1 * torch.randn(hd, generator=g)).to(torch.bfloat16).to(DEV)
+    kw = (1 + 0.1 * torch.randn(hd, generator=g)).to(torch.bfloat16).to(DEV)
+    say(f"[rope forms] hd={hd} trad={trad} {trn.describe_rope(trn.BF16, hd, hd, trad, variant=0)}")
+    a = trn.dual_head_rms_rope(q, k, qw, kw, 1e-6, traditional=trad, offset=77, variant=0)
+    b = trn.dual_head_rms_rope(q, k, qw, kw, 1e-6, traditional=trad, offset=77, variant=1)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
 def test_special_rows(o):
     """Zero rows, constant rows, NaN and infinity propagate as the oracle says."""
     for dtype in (torch.float32, torch.bfloat16, torch.float16):
