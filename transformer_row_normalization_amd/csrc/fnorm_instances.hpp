@@ -149,7 +149,10 @@ inline void add_masked(std::vector<Variant>& t) {
     add_shape<DT, V, 4, 256, 256, true, WIDE_NT>(t, WIDE_CAP, 4 * R);
     add_shape<DT, V, 8, 256, 256, true, WIDE_NT>(t, WIDE_CAP, 3 * R);
     if constexpr (V > 1) add_shape<DT, V, 6, 512, 512, true, WIDE_NT>(t, WIDE_CAP, 2);
-    add_shape<DT, V, 4, 1024, 1024, true, WIDE_NT>(t);
+    // one 1024-thread workgroup per CU: with 32-bit pack offsets the fp32
+    // and fp16 RMSNorm kernels fit two, which took RMSNorm at fp32 16384
+    // from 91.5 to 106.8 us
+    add_shape<DT, V, 4, 1024, 1024, true, WIDE_NT>(t, V > 1 ? 1 : 0);
     if constexpr (V > 1) add_shape<DT, V, 16, 512, 512, true, WIDE_NT, KM_LAYER_BIAS>(t);
     add_shape<DT, V, 8, 1024, 1024, true, WIDE_NT>(t);
 }
@@ -209,9 +212,10 @@ inline void register_dtype(std::vector<Variant>& t) {
     FNORM_EXACT(4, 32, 256, NT_BOTH, 2)
     FNORM_EXACT(2, 64, 256, NT_BOTH, 2)
     FNORM_EXACT(2, 64, 256, NT_NONE, 0)
-    // 192 packs (f32 768)
-    FNORM_EXACT(3, 64, 256, NT_NONE, 0)
+    // 192 packs (f32 768, bf16 1536): non-temporal, 2 workgroups per CU,
+    // 16-20% faster over 256 MiB than ordinary access at full occupancy
     FNORM_EXACT(3, 64, 256, NT_BOTH, 2)
+    FNORM_EXACT(3, 64, 256, NT_NONE, 0)
     // 256 packs (f32 1024, bf16 2048)
     FNORM_EXACT(4, 64, 256, NT_BOTH, 2)
     FNORM_EXACT(2, 128, 256, NT_BOTH, 2)
