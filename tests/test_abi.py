@@ -168,8 +168,11 @@ def test_launch_policy_and_per_kind_order():
         assert trn.describe(trn.OP_LAYER, BF16, w) == "layer.bf16.vec8.vpt2.lpr32.blk256.masked.nt.grid"
     assert trn.describe(trn.OP_RMS, BF16, 200) == "rms.bf16.vec8.vpt1.lpr32.blk256.masked.persistent"
     for w in (18432, 24576):
-        d = trn.describe(trn.OP_LAYER, BF16, w)
-        assert d.startswith("layer.bf16.vec8.vpt6.lpr512.blk512.masked.nt.") and d.endswith(".grid2"), d
+        d = trn.describe(trn.OP_RMS, BF16, w)
+        assert d.startswith("rms.bf16.vec8.vpt6.lpr512.blk512.masked.nt.") and d.endswith(".grid2"), d
+    # LayerNorm with a bias there: exact shapes of 9 and 12 packs per lane
+    assert trn.describe(trn.OP_LAYER, BF16, 18432) == "layer.bf16.vec8.vpt9.lpr256.blk256.exact.nt.grid"
+    assert trn.describe(trn.OP_LAYER, BF16, 24576) == "layer.bf16.vec8.vpt12.lpr256.blk256.exact.nt.grid"
     # one row per 1024-thread workgroup: persistent first
     for w in (32768, 40000):
         d = trn.describe(trn.OP_RMS, BF16, w)
