@@ -203,6 +203,7 @@ def test_launch_policy_and_per_kind_order():
     assert trn.describe(trn.OP_DUAL, BF16, 128) == "dual.bf16.vec8.vpt2.lpr8.blk256.exact.nt.grid"
     assert trn.describe(trn.OP_DUAL, BF16, 256) == "dual.bf16.vec8.vpt1.lpr32.blk256.exact.nt.grid"
     assert trn.describe(trn.OP_DUAL, F32, 128) == "dual.f32.vec4.vpt1.lpr32.blk256.exact.nt.grid"
+    assert trn.describe(trn.OP_DUAL, BF16, 192) == "dual.bf16.vec8.vpt3.lpr8.blk256.exact.nt.grid"
     assert trn.describe(trn.OP_DUAL, BF16, 128, variant=1) == "dual.bf16.vec8.vpt2.lpr8.blk256.exact.nt.persistent"
     # 4-8 packs per lane at 128, 256 and 2048 packs
     assert ".vpt4.lpr32." in trn.describe(trn.OP_LAYER, BF16, 1024)
