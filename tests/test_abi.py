@@ -162,7 +162,7 @@ def test_launch_policy_and_per_kind_order():
             assert d1.rsplit(".", 1)[0] == d.rsplit(".", 1)[0] and ".persistent" in d1, d1
     assert trn.describe(trn.OP_RMS, BF16, 5120).startswith("rms.bf16.vec8.vpt5.lpr128.")
     # the shortest masked rows run without a limit
-    assert trn.describe(trn.OP_RMS, BF16, 640).endswith(".masked.nt.grid")
+    assert trn.describe(trn.OP_RMS, BF16, 656).endswith(".masked.nt.grid")
     # 33-64 packs: 2 packs per lane on a plain grid; fewer: one pack, persistent
     for w in (264, 320, 504):
         assert trn.describe(trn.OP_LAYER, BF16, w) == "layer.bf16.vec8.vpt2.lpr32.blk256.masked.nt.grid"
@@ -204,6 +204,8 @@ def test_launch_policy_and_per_kind_order():
     assert trn.describe(trn.OP_DUAL, BF16, 256) == "dual.bf16.vec8.vpt1.lpr32.blk256.exact.nt.grid"
     assert trn.describe(trn.OP_DUAL, F32, 128) == "dual.f32.vec4.vpt1.lpr32.blk256.exact.nt.grid"
     assert trn.describe(trn.OP_DUAL, BF16, 192) == "dual.bf16.vec8.vpt3.lpr8.blk256.exact.nt.grid"
+    assert trn.describe(trn.OP_LAYER, BF16, 576) == "layer.bf16.vec8.vpt9.lpr8.blk256.exact.nt.grid"
+    assert trn.describe(trn.OP_LAYER, BF16, 640) == "layer.bf16.vec8.vpt5.lpr16.blk256.exact.nt.grid"
     assert trn.describe(trn.OP_DUAL, BF16, 128, variant=1) == "dual.bf16.vec8.vpt2.lpr8.blk256.exact.nt.persistent"
     # 4-8 packs per lane at 128, 256 and 2048 packs
     assert ".vpt4.lpr32." in trn.describe(trn.OP_LAYER, BF16, 1024)

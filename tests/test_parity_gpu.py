@@ -168,7 +168,8 @@ VARIANT_CASES = [("rms", torch.bfloat16, 128), ("rms", torch.bfloat16, 768),
                  ("layer", torch.float32, 24576), ("layer", torch.bfloat16, 360),
                  ("rms", torch.float32, 180), ("layer", torch.bfloat16, 6144),
                  ("layer", torch.float32, 3000), ("layer", torch.bfloat16, 24576),
-                 ("layer", torch.bfloat16, 192), ("rms", torch.float32, 96)]
+                 ("layer", torch.bfloat16, 192), ("rms", torch.float32, 96),
+                 ("layer", torch.bfloat16, 576), ("layer", torch.float32, 320)]
 
 
 @pytest.mark.parametrize("op,dtype,width", VARIANT_CASES,
