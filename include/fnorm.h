@@ -57,11 +57,16 @@ typedef enum {
     FNORM_ERR_WORKSPACE = 8    /* workspace NULL, misaligned, too small or overlapping */
 } fnorm_status;
 
+/* Operation codes of the introspection calls (fnorm_variant_count,
+ * fnorm_describe_shape, fnorm_describe).  LayerNorm with a bias and without
+ * one run different kernels: FNORM_OP_LAYER names the first, except in
+ * fnorm_describe, where the call's own b pointer decides. */
 typedef enum {
     FNORM_OP_RMS = 0,
     FNORM_OP_LAYER = 1,
     FNORM_OP_DUAL = 2,
-    FNORM_OP_RMS_SWIGLU = 3
+    FNORM_OP_RMS_SWIGLU = 3,
+    FNORM_OP_LAYER_NOBIAS = 4
 } fnorm_op;
 
 /*
@@ -214,23 +219,58 @@ int fnorm_dual_head_rms_rope_strided(const void* q, int64_t q_stride, const void
                                      const float* freqs, int dtype, void* stream, int variant);
 
 /*
- * Number of kernel variants able to serve (op, dtype, width) when every
- * pointer is 16-byte aligned (aligned != 0) or not.  Returns 0 for invalid
- * arguments.  Host-only: makes no HIP call.
+ * Introspection: which kernel, and which launch form, a call takes.  A silent
+ * slow path counts as a failure on the pages (the Emily notebook, Part 1,
+ * compiles with native_fallback: :raise, so an op that cannot run natively
+ * raises); these calls let a caller assert the path a concrete call takes.
+ * Names look like "layer.bf16.vec8.vpt4.lpr128.blk256.exact.nt.persistent2":
+ * operation, element type, elements per access (1 = the scalar-access kernel
+ * taken for misaligned pointers, strides or widths), packs per thread,
+ * threads per row, threads per workgroup, exact or masked width, cache
+ * policy (".nt" non-temporal loads and stores, ".ntld" loads only, ".ntst"
+ * stores only), and the launch: "persistent" (as many workgroups as fit),
+ * "persistentK" (K per CU), "grid" (one workgroup per block of rows) or
+ * "gridK" (the same, at most K resident per CU).  "wide" kernels make
+ * several passes over rows wider than the register-resident capacity.
+ * All of them are host-only: they make no HIP call.
+ *
+ * fnorm_describe, fnorm_describe_dual, fnorm_describe_dual_rope take the
+ * arguments of the call they describe (strides in elements as in the
+ * _strided forms; a contiguous call passes its width, or heads * head_dim,
+ * and strides are ignored for a single row or token) and run that call's
+ * validation and kernel choice without launching it: they return the status
+ * the call would return (FNORM_ERR_* before any launch) and write the name
+ * of the kernel it would launch, or "none" for a call that launches nothing
+ * (no rows).  eps is not an argument (it does not affect the choice).
+ *   fnorm_describe: op FNORM_OP_RMS (g and b ignored), FNORM_OP_LAYER (b may
+ *     be NULL: the no-bias kernels), FNORM_OP_LAYER_NOBIAS (b ignored) or
+ *     FNORM_OP_RMS_SWIGLU (g the gate, b ignored); other ops return
+ *     FNORM_ERR_UNSUPPORTED.
+ * fnorm_describe_shape names variant `variant` (-1 = default) for (op,
+ * dtype, width) when every pointer and stride is 16-byte aligned
+ * (aligned != 0) or not, and fnorm_variant_count counts those variants (0
+ * for invalid arguments); variant as for the _v calls.
+ * Each writes at most len bytes to buf (NUL-terminated); FNORM_ERR_NULL if
+ * buf is NULL or len <= 0.
  */
 int fnorm_variant_count(int op, int dtype, int64_t width, int aligned);
-
-/*
- * Writes into buf (NUL-terminated, at most len bytes) the name of the kernel
- * and launch shape that variant `variant` (-1 = default) of (op, dtype,
- * width, aligned) uses, e.g. "rms.bf16.vec8.vpt4.lpr256.blk256.exact.persistent".
- * The last field is the launch: "persistent" (as many workgroups as fit),
- * "persistentK" (K workgroups per CU), "grid" (one workgroup per block of
- * rows) or "gridK" (the same, with at most K workgroups resident per CU).
- * Returns FNORM_OK, FNORM_ERR_UNSUPPORTED or FNORM_ERR_NULL.  Host-only.
- */
-int fnorm_describe(int op, int dtype, int64_t width, int aligned, int variant, char* buf,
-                   int64_t len);
+int fnorm_describe_shape(int op, int dtype, int64_t width, int aligned, int variant, char* buf,
+                         int64_t len);
+int fnorm_describe(int op, const void* x, int64_t x_stride, const void* g, int64_t g_stride,
+                   const void* w, const void* b, const void* y, int64_t y_stride, int64_t rows,
+                   int64_t width, int dtype, int variant, char* buf, int64_t len);
+int fnorm_describe_dual(const void* q, int64_t q_stride, const void* k, int64_t k_stride,
+                        const void* qw, const void* kw, const void* qy, int64_t qy_stride,
+                        const void* ky, int64_t ky_stride, int64_t tokens, int64_t q_heads,
+                        int64_t k_heads, int64_t head_dim, int dtype, int variant, char* buf,
+                        int64_t len);
+int fnorm_describe_dual_rope(const void* q, int64_t q_stride, const void* k, int64_t k_stride,
+                             const void* qw, const void* kw, const void* qy, int64_t qy_stride,
+                             const void* ky, int64_t ky_stride, int64_t tokens, int64_t q_heads,
+                             int64_t k_heads, int64_t head_dim, int64_t rope_dims,
+                             int traditional, float base, float scale, int64_t offset,
+                             const float* freqs, int dtype, int variant, char* buf,
+                             int64_t len);
 
 /*
  * Composed (unfused) baselines: the same RMSNorm / LayerNorm computed one
@@ -261,11 +301,20 @@ int fnorm_rope_variant_count(int dtype, int64_t head_dim, int64_t rope_dims, int
 int fnorm_describe_rope(int dtype, int64_t head_dim, int64_t rope_dims, int traditional,
                         int aligned, int variant, char* buf, int64_t len);
 
-/* Static text of a status code. */
+/*
+ * Errors follow the error type of mlx-c-rust `compile/norm_fusion.rs` (the
+ * dual head-norm graph builder and its callers): a failed call reports an
+ * operation name plus a description, and structural checks (input and output
+ * counts there; pointers, sizes, overlaps here) run before any work.
+ *
+ * fnorm_status_string: static text of a status code ("unknown fnorm status"
+ * for codes outside fnorm_status); never NULL.
+ * fnorm_last_error: the text of the last error on the calling thread,
+ * "operation: description" (e.g. "fnorm_rms: rows=-1 width=8 (need rows >=
+ * 0, width > 0)"), or "" if the thread's last fnorm call succeeded.  The
+ * storage is per thread and valid until that thread's next fnorm call.
+ */
 const char* fnorm_status_string(int status);
-
-/* Text of the last error on the calling thread ("operation: description"),
- * or "" if the last call succeeded. */
 const char* fnorm_last_error(void);
 
 /* Library version, as major * 10000 + minor * 100 + patch. */

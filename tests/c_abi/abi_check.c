@@ -48,12 +48,25 @@ int main(void)
     expect("composed ws", fnorm_rms_composed(x, w, y, 4, 8, 1e-6f, FNORM_F32, NULL, 0, NULL),
            FNORM_ERR_WORKSPACE);
     expect("copy size", fnorm_bench_copy(x, y, 24, NULL), FNORM_ERR_SHAPE);
-    expect("describe", fnorm_describe(FNORM_OP_RMS, FNORM_BF16, 8192, 1, -1, buf, sizeof buf),
+    expect("describe shape", fnorm_describe_shape(FNORM_OP_RMS, FNORM_BF16, 8192, 1, -1, buf,
+                                                  sizeof buf),
            FNORM_OK);
     if (strncmp(buf, "rms.bf16.", 9) != 0) {
+        fprintf(stderr, "describe_shape gave '%s'\n", buf);
+        ++failures;
+    }
+    /* the call form: a misaligned x takes the scalar-access kernel */
+    expect("describe call", fnorm_describe(FNORM_OP_LAYER, (char *)x + 2, 8192, NULL, 0, w, NULL,
+                                           y, 8192, 4, 8192, FNORM_BF16, -1, buf, sizeof buf),
+           FNORM_OK);
+    if (strncmp(buf, "layer.bf16.vec1.", 16) != 0) {
         fprintf(stderr, "describe gave '%s'\n", buf);
         ++failures;
     }
+    expect("describe call error", fnorm_describe(FNORM_OP_RMS, x, 8, NULL, 0, w, NULL,
+                                                 (char *)x + 16, 8, 4, 8, FNORM_F32, -1, buf,
+                                                 sizeof buf),
+           FNORM_ERR_ALIAS);
     if (fnorm_variant_count(FNORM_OP_DUAL, FNORM_BF16, 128, 1) < 2) ++failures;
     if (fnorm_version() < 100) ++failures;
     if (failures == 0) printf("c abi ok (version %d)\n", fnorm_version());

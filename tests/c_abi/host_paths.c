@@ -40,18 +40,19 @@ static void tables(void)
                                      64,   100,  128,  255,  256,  768,  1000,  1024, 2048,
                                      4096, 4097, 8192, 8193, 20000, 65536, 65537, 1 << 20};
     char big[256], tiny[4];
-    for (int op = -1; op <= 4; ++op)
+    for (int op = -1; op <= 5; ++op)
         for (int dt = -1; dt <= 3; ++dt)
             for (size_t i = 0; i < sizeof widths / sizeof widths[0]; ++i)
                 for (int al = 0; al <= 1; ++al) {
                     const int n = fnorm_variant_count(op, dt, widths[i], al);
                     CHECK(n >= 0);
                     for (int v = -1; v <= n; ++v) {
-                        const int s = fnorm_describe(op, dt, widths[i], al, v, big, sizeof big);
-                        const int valid = op >= 0 && op <= 3 && dt >= 0 && dt <= 2;
+                        const int s = fnorm_describe_shape(op, dt, widths[i], al, v, big,
+                                                           sizeof big);
+                        const int valid = op >= 0 && op <= 4 && dt >= 0 && dt <= 2;
                         CHECK(!(valid && n > 0 && v < n && s != FNORM_OK));
                         CHECK(s != FNORM_OK || strlen(big) < sizeof big);
-                        (void)fnorm_describe(op, dt, widths[i], al, v, tiny, sizeof tiny);
+                        (void)fnorm_describe_shape(op, dt, widths[i], al, v, tiny, sizeof tiny);
                         CHECK(strlen(tiny) < sizeof tiny);
                     }
                 }
@@ -66,8 +67,40 @@ static void tables(void)
                             (void)fnorm_describe_rope(dt, hd, dims, trad, al, v, tiny, 1);
                         }
                     }
-    EXPECT("describe null buf", fnorm_describe(0, 1, 128, 1, -1, NULL, 8), FNORM_ERR_NULL);
-    EXPECT("describe zero len", fnorm_describe(0, 1, 128, 1, -1, big, 0), FNORM_ERR_NULL);
+    EXPECT("describe null buf", fnorm_describe_shape(0, 1, 128, 1, -1, NULL, 8), FNORM_ERR_NULL);
+    EXPECT("describe zero len", fnorm_describe_shape(0, 1, 128, 1, -1, big, 0), FNORM_ERR_NULL);
+    EXPECT("describe call null buf", fnorm_describe(0, (void *)0x1000, 8, NULL, 0, (void *)0x2000,
+                                                    NULL, (void *)0x3000, 8, 1, 8, 1, -1, NULL,
+                                                    8),
+           FNORM_ERR_NULL);
+    /* a LayerNorm without bias has its own kernel list (fewer shapes at some
+       widths): the shape query of FNORM_OP_LAYER_NOBIAS and the call with
+       b == NULL agree */
+    {
+        static const int64_t nb_widths[] = {6144, 18432, 24576, 65536, 4096, 768};
+        for (size_t i = 0; i < sizeof nb_widths / sizeof nb_widths[0]; ++i) {
+            char a[256], c[256];
+            const int n = fnorm_variant_count(FNORM_OP_LAYER_NOBIAS, FNORM_BF16, nb_widths[i], 1);
+            CHECK(n >= 2);
+            for (int v = -1; v < n; ++v) {
+                EXPECT("nobias shape", fnorm_describe_shape(FNORM_OP_LAYER_NOBIAS, FNORM_BF16,
+                                                            nb_widths[i], 1, v, a, sizeof a),
+                       FNORM_OK);
+                EXPECT("nobias call", fnorm_describe(FNORM_OP_LAYER, (void *)0x100000, nb_widths[i],
+                                                     NULL, 0, (void *)0x20000000, NULL,
+                                                     (void *)0x40000000, nb_widths[i], 16,
+                                                     nb_widths[i], FNORM_BF16, v, c, sizeof c),
+                       FNORM_OK);
+                CHECK(strcmp(a, c) == 0);
+            }
+            /* one past the last no-bias variant is refused by the call too */
+            EXPECT("nobias past end", fnorm_describe(FNORM_OP_LAYER, (void *)0x100000,
+                                                     nb_widths[i], NULL, 0, (void *)0x20000000,
+                                                     NULL, (void *)0x40000000, nb_widths[i], 16,
+                                                     nb_widths[i], FNORM_BF16, n, c, sizeof c),
+                   FNORM_ERR_UNSUPPORTED);
+        }
+    }
     for (int s = -2; s <= 10; ++s)
         CHECK(fnorm_status_string(s) != NULL);
 }
@@ -125,6 +158,39 @@ static void entry_points(void)
     EXPECT("rms rows", fnorm_rms(A, B, C, -1, 8, 1e-6f, FNORM_F32, NULL), FNORM_ERR_SHAPE);
     EXPECT("rms overflow", fnorm_rms(A, B, C, INT64_MAX / 4, 64, 1e-6f, FNORM_F32, NULL),
            FNORM_ERR_SHAPE);
+    /* row counts whose product with head_dim overflows int64: rejected, and
+       no overflowing product is formed on the way (UBSan watches) */
+    EXPECT("dual overflow", fnorm_dual_head_rms(A, D, B, E, C, F, INT64_MAX / 4, 1, 128, 1e-6f,
+                                                FNORM_BF16, NULL),
+           FNORM_ERR_SHAPE);
+    EXPECT("dual overflow k", fnorm_dual_head_rms(A, D, B, E, C, F, 1, INT64_MAX / 4, 128, 1e-6f,
+                                                  FNORM_BF16, NULL),
+           FNORM_ERR_SHAPE);
+    EXPECT("rope overflow", fnorm_dual_head_rms_rope(A, D, B, E, C, F, 4, INT64_MAX / 4, 1, 128,
+                                                     1e-6f, 128, 0, 10000.0f, 1.0f, 0, NULL,
+                                                     FNORM_BF16, NULL),
+           FNORM_ERR_SHAPE);
+    {
+        char nb[64];
+        EXPECT("describe dual overflow", fnorm_describe_dual(A, 0, D, 0, B, E, C, 0, F, 0, 1,
+                                                             INT64_MAX / 4, 1, 128, FNORM_BF16,
+                                                             -1, nb, sizeof nb),
+               FNORM_ERR_SHAPE);
+        EXPECT("describe dual call", fnorm_describe_dual(A, 0, D, 0, B, E, C, 0, F, 0, 1, 4096, 1024,
+                                                         128, FNORM_BF16, -1, nb, sizeof nb),
+               FNORM_OK);
+        CHECK(strncmp(nb, "dual.bf16.vec8.", 15) == 0);
+        EXPECT("describe rope call", fnorm_describe_dual_rope(
+                                         A, 32 * 128, D, 8 * 128, B, E, C, 32 * 128, F, 8 * 128,
+                                         16, 32, 8, 128, 128, 0, 10000.0f, 1.0f, 0, NULL,
+                                         FNORM_BF16, -1, nb, sizeof nb),
+               FNORM_OK);
+        CHECK(strncmp(nb, "ropesplit.bf16.", 15) == 0);
+        EXPECT("describe no rows", fnorm_describe(FNORM_OP_RMS, NULL, 8, NULL, 0, NULL, NULL, NULL,
+                                                  8, 0, 8, FNORM_F32, -1, nb, sizeof nb),
+               FNORM_OK);
+        CHECK(strcmp(nb, "none") == 0);
+    }
     EXPECT("rms eps", fnorm_rms(A, B, C, 4, 8, -0.5f, FNORM_F32, NULL), FNORM_ERR_EPS);
     EXPECT("dual heads", fnorm_dual_head_rms_strided(A, 64, D, 64, B, E, C, 64, F, 64, 4, -1, 1,
                                                      64, 1e-6f, FNORM_BF16, NULL, -1),

@@ -81,8 +81,8 @@ def test_row_strided_matches_oracle_and_contiguous(o, case, dtype):
     assert got.data_ptr() == y.data_ptr()
     ref = run(op, t["x"].to(DEV), w, b, 1e-5)
     torch.cuda.synchronize()
-    helpers.check(op, y.cpu(), oracle_rows(o, op, t["x"], t["w"], t.get("b"), 1e-5), t["w"],
-                  f"strided {op} {width}")
+    helpers.check_row(op, y.cpu(), oracle_rows(o, op, t["x"], t["w"], t.get("b"), 1e-5),
+                      t["w"], t.get("b"), f"strided {op} {width}")
     aligned = (xs * eb) % 16 == 0 and (ys * eb) % 16 == 0 and (xc * eb) % 16 == 0 \
         and (yc * eb) % 16 == 0
     if aligned:   # the same kernel as the contiguous call
@@ -119,7 +119,7 @@ def test_row_strided_every_variant(o, op):
         y = ybuf[:, 512:512 + width]
         run(op, x, w, b, 1e-5, out=y, variant=v)
         torch.cuda.synchronize()
-        helpers.check(op, y.cpu(), r, t["w"], f"strided {op} v{v}")
+        helpers.check_row(op, y.cpu(), r, t["w"], t.get("b"), f"strided {op} v{v}")
         assert torch.all(ybuf[:, :512].cpu() == 0) and torch.all(ybuf[:, 512 + width:].cpu() == 0)
 
 
@@ -204,20 +204,10 @@ def test_packed_qkv_rope_in_place(o, case):
         torch.cuda.synchronize()
         rq, rk = o.dual_head_rms_rope(*(helpers.to_oracle_array(t.cpu()) for t in (q0, k0, qw, kw)),
                                       1e-6, hd, trad, 10000.0, 1.0, 37)
-        helpers.check("rms", q.cpu(), rq, label="packed rope q", floor=rope_floor(qw, hd, trad))
-        helpers.check("rms", k.cpu(), rk, label="packed rope k", floor=rope_floor(kw, hd, trad))
+        helpers.check_rope(o, q0.cpu(), k0.cpu(), qw.cpu(), kw.cpu(), q.cpu(), k.cpu(), rq, rk,
+                           hd, trad, "packed rope", (37 + tokens) / (2 * np.pi))
         assert torch.equal(bits(q), bits(ref_q)) and torch.equal(bits(k), bits(ref_k))
         assert torch.equal(bits(v), bits(v0))
-
-
-def rope_floor(w, dims, traditional):
-    wd = np.abs(helpers.widen(w))
-    f = wd.copy()
-    half = dims // 2
-    for i in range(half):
-        a, b = (2 * i, 2 * i + 1) if traditional else (i, i + half)
-        f[a] = f[b] = max(wd[a], wd[b])
-    return f
 
 
 def test_packed_qkv_to_separate_outputs(o):

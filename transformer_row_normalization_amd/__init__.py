@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(HERE, "libfnorm.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "fnorm.h")
 
 F32, BF16, F16 = 0, 1, 2
-OP_RMS, OP_LAYER, OP_DUAL, OP_RMS_SWIGLU = 0, 1, 2, 3
+OP_RMS, OP_LAYER, OP_DUAL, OP_RMS_SWIGLU, OP_LAYER_NOBIAS = 0, 1, 2, 3, 4
 STATUS = {0: "FNORM_OK", 1: "FNORM_ERR_NULL", 2: "FNORM_ERR_SHAPE", 3: "FNORM_ERR_EPS",
           4: "FNORM_ERR_DTYPE", 5: "FNORM_ERR_ALIAS", 6: "FNORM_ERR_UNSUPPORTED",
           7: "FNORM_ERR_LAUNCH", 8: "FNORM_ERR_WORKSPACE"}
@@ -54,7 +54,14 @@ _SIGNATURES = {
     "fnorm_layer_v": ([_P, _P, _P, _P, _I64, _I64, _F, _I, _P, _I], _I),
     "fnorm_dual_head_rms_v": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _F, _I, _P, _I], _I),
     "fnorm_variant_count": ([_I, _I, _I64, _I], _I),
-    "fnorm_describe": ([_I, _I, _I64, _I, _I, ctypes.c_char_p, _I64], _I),
+    "fnorm_describe_shape": ([_I, _I, _I64, _I, _I, ctypes.c_char_p, _I64], _I),
+    "fnorm_describe": ([_I, _P, _I64, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I, _I,
+                        ctypes.c_char_p, _I64], _I),
+    "fnorm_describe_dual": ([_P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _I64, _I64, _I64, _I64,
+                             _I64, _I, _I, ctypes.c_char_p, _I64], _I),
+    "fnorm_describe_dual_rope": ([_P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _I64, _I64, _I64,
+                                  _I64, _I64, _I64, _I, _F, _F, _I64, _P, _I, _I,
+                                  ctypes.c_char_p, _I64], _I),
     "fnorm_status_string": ([_I], ctypes.c_char_p),
     "fnorm_last_error": ([], ctypes.c_char_p),
     "fnorm_version": ([], _I),
@@ -426,8 +433,52 @@ def variant_count(op: int, dtype_code: int, width: int, aligned: bool = True) ->
 
 
 def describe(op: int, dtype_code: int, width: int, aligned: bool = True, variant: int = -1) -> str:
+    """Kernel name of variant `variant` (-1: default) for (op, dtype, width)
+    with every pointer 16-byte aligned or not (no tensors needed)."""
     buf = ctypes.create_string_buffer(256)
-    _check(lib().fnorm_describe(op, dtype_code, width, 1 if aligned else 0, variant, buf, 256))
+    _check(lib().fnorm_describe_shape(op, dtype_code, width, 1 if aligned else 0, variant, buf,
+                                      256))
+    return buf.value.decode()
+
+
+def describe_call(op: int, x, w, b=None, out=None, g=None, variant: int = -1) -> str:
+    """Kernel name the row call op(x, [g,] w, [b,] out=out) would launch, from
+    the library's own validation and choice for these tensors (alignment,
+    strides, in place, bias present); raises what the call would raise."""
+    y = x if out is None else out
+    width = x.shape[-1] if x.dim() else 1
+    rows = x.numel() // width if width else 0
+    xs = _row_stride(x, "x") if rows > 1 else width
+    ys = _row_stride(y, "out") if rows > 1 else width
+    gs = (_row_stride(g, "g") if rows > 1 else width) if g is not None else 0
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().fnorm_describe(op, _ptr(x), xs, _ptr(g), gs, _ptr(w), _ptr(b), _ptr(y), ys,
+                                rows, width, _dtype_code(x), variant, buf, 256))
+    return buf.value.decode()
+
+
+def describe_dual_call(q, k, qw, kw, q_out=None, k_out=None, variant: int = -1,
+                       rope: dict | None = None) -> str:
+    """Kernel name the dual call on [tokens, heads, head_dim] tensors would
+    launch (with `rope`, a dict of dims, traditional, base, scale, offset,
+    freqs: the fused RoPE call)."""
+    qy = q if q_out is None else q_out
+    ky = k if k_out is None else k_out
+    tokens, qh, hd = q.shape
+    kh = k.shape[1]
+    qs, ks = _token_stride(q, "q"), _token_stride(k, "k")
+    qys, kys = _token_stride(qy, "q_out"), _token_stride(ky, "k_out")
+    buf = ctypes.create_string_buffer(256)
+    if rope is None:
+        _check(lib().fnorm_describe_dual(_ptr(q), qs, _ptr(k), ks, _ptr(qw), _ptr(kw), _ptr(qy),
+                                         qys, _ptr(ky), kys, tokens, qh, kh, hd,
+                                         _dtype_code(q), variant, buf, 256))
+    else:
+        _check(lib().fnorm_describe_dual_rope(
+            _ptr(q), qs, _ptr(k), ks, _ptr(qw), _ptr(kw), _ptr(qy), qys, _ptr(ky), kys, tokens,
+            qh, kh, hd, rope.get("dims", hd), int(rope.get("traditional", False)),
+            rope.get("base", 10000.0), rope.get("scale", 1.0), rope.get("offset", 0),
+            _ptr(rope.get("freqs")), _dtype_code(q), variant, buf, 256))
     return buf.value.decode()
 
 

@@ -257,9 +257,12 @@ bool pick(int kind, int dt, int64_t width, bool aligned, int variant, Choice* c)
 int op_kind(int op, bool has_bias) {
     if (op == FNORM_OP_RMS) return K_RMS;
     if (op == FNORM_OP_LAYER) return has_bias ? K_LAYER : K_LAYER_NOBIAS;
+    if (op == FNORM_OP_LAYER_NOBIAS) return K_LAYER_NOBIAS;
     if (op == FNORM_OP_RMS_SWIGLU) return K_RMS_GATED;
     return K_DUAL;
 }
+
+bool valid_op(int op) { return op >= FNORM_OP_RMS && op <= FNORM_OP_LAYER_NOBIAS; }
 
 void describe_choice(const Choice& c, char* buf, size_t len) {
     const Variant& v = *c.v;
@@ -285,6 +288,13 @@ void describe_choice(const Choice& c, char* buf, size_t len) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// a * b <= INT64_MAX / 8 for non-negative a, b; negative values pass (the
+// checks that follow reject them with their own message).
+bool product_fits(int64_t a, int64_t b) {
+    if (a <= 0 || b <= 0) return true;
+    return a <= (INT64_MAX / 8) / b;
+}
 
 bool overlap(const void* a, int64_t an, const void* b, int64_t bn) {
     if (!a || !b || an <= 0 || bn <= 0) return false;
@@ -419,10 +429,11 @@ int launch(const char* op, const Choice& c, NormArgs& a, void* stream) {
     if (grid > (int64_t(1) << 30)) grid = int64_t(1) << 30;  // grid-stride covers the rest
     const int lds = !c.persistent && c.v->grid_resident > 0 ? resident_lds(c.v) : 0;
     void* args[] = {&a};
-    hipError_t e = hipLaunchKernel(c.v->fn, dim3(unsigned(grid)), dim3(unsigned(c.v->block)),
-                                   args, size_t(lds), static_cast<hipStream_t>(stream));
-    hipError_t e2 = hipGetLastError();
-    if (e == hipSuccess) e = e2;
+    // The launch's own status only: the thread's last-error slot may hold an
+    // earlier, unrelated failure of the caller's, which is not this call's.
+    const hipError_t e = hipLaunchKernel(c.v->fn, dim3(unsigned(grid)),
+                                         dim3(unsigned(c.v->block)), args, size_t(lds),
+                                         static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(FNORM_ERR_LAUNCH, op, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -468,9 +479,12 @@ bool output_clashes(const Span& y, const Span& x) {
 bool stride_aligned(int64_t stride_elems, int64_t eb) { return (stride_elems * eb) % 16 == 0; }
 
 // RMSNorm / LayerNorm over rows addressed with row strides (elements).
+// With `plan` set, nothing is launched: the call is validated and its kernel
+// choice returned there (plan->v == nullptr when the call launches nothing).
 int rows_impl(const char* op, int fop, const void* x, int64_t xs, const void* g, int64_t gs,
               const void* w, const void* b, void* y, int64_t ys, int64_t rows, int64_t width,
-              float eps, int dtype, void* stream, int variant) {
+              float eps, int dtype, void* stream, int variant, Choice* plan = nullptr) {
+    if (plan) plan->v = nullptr;
     const bool gated = fop == FNORM_OP_RMS_SWIGLU;
     if (int s = check_scalars(op, dtype, rows, width, eps)) return s;
     if (rows > 1 && (xs < width || ys < width || (gated && gs < width)))
@@ -501,6 +515,10 @@ int rows_impl(const char* op, int fop, const void* x, int64_t xs, const void* g,
     if (!pick(kind, dtype, width, al, variant, &c))
         return fail(FNORM_ERR_UNSUPPORTED, op, "no kernel variant %d for width %lld", variant,
                     (long long)width);
+    if (plan) {
+        *plan = c;
+        return ok();
+    }
     NormArgs a{x,    w,    b,     y,     nullptr, nullptr, nullptr, rows, rows, width,
                eps,  one ? width : xs, one ? width : ys, 1, width, width, 1,
                gated ? g : nullptr, one ? width : gs};
@@ -560,7 +578,8 @@ int dual_checks(const char* op, const void* q, int64_t qs, const void* k, int64_
 int dual_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t ks,
               const void* qw, const void* kw, void* qy, int64_t qys, void* ky, int64_t kys,
               int64_t tokens, int64_t q_heads, int64_t k_heads, int64_t head_dim, float eps,
-              int dtype, void* stream, int variant) {
+              int dtype, void* stream, int variant, Choice* plan = nullptr) {
+    if (plan) plan->v = nullptr;
     bool al = false;
     if (int s = dual_checks(op, q, qs, k, ks, qw, kw, qy, qys, ky, kys, tokens, q_heads, k_heads,
                             head_dim, eps, dtype, nullptr, 0, &al))
@@ -571,6 +590,10 @@ int dual_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
     if (!pick(K_DUAL, dtype, head_dim, al, variant, &c))
         return fail(FNORM_ERR_UNSUPPORTED, op, "no kernel variant %d for head_dim %lld", variant,
                     (long long)head_dim);
+    if (plan) {
+        *plan = c;
+        return ok();
+    }
     // A side with no rows is never read; give the kernel the other side's
     // valid weight pointer so its register preload stays in bounds.
     const void* qw_eff = q_rows > 0 ? qw : kw;
@@ -594,7 +617,8 @@ int rope_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
               const void* qw, const void* kw, void* qy, int64_t qys, void* ky, int64_t kys,
               int64_t tokens, int64_t q_heads, int64_t k_heads, int64_t head_dim, float eps,
               int64_t rope_dims, int traditional, float base, float scale, int64_t offset,
-              const float* freqs, int dtype, void* stream, int variant) {
+              const float* freqs, int dtype, void* stream, int variant, Choice* plan = nullptr) {
+    if (plan) plan->v = nullptr;
     if (rope_dims < 2 || rope_dims % 2 != 0 || rope_dims > head_dim)
         return fail(FNORM_ERR_SHAPE, op, "rope_dims=%lld must be even and in [2, head_dim=%lld]",
                     (long long)rope_dims, (long long)head_dim);
@@ -622,6 +646,11 @@ int rope_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
                     (long long)head_dim, (long long)rope_dims, variant);
     const Variant* v = list[variant / 2];
     const bool persistent = (variant % 2 == 0) != v->grid_first;
+    if (plan) {
+        plan->v = v;
+        plan->persistent = persistent;
+        return ok();
+    }
     const void* qw_eff = q_rows > 0 ? qw : kw;
     const void* kw_eff = k_rows > 0 ? kw : qw;
     RopeArgs ra{NormArgs{q, qw_eff, nullptr, qy, k, kw_eff, ky, q_rows + k_rows, q_rows,
@@ -649,10 +678,8 @@ int rope_impl(const char* op, const void* q, int64_t qs, const void* k, int64_t 
     ra.q_blocks = uint32_t(gq);
     const int64_t grid = gq + gk;
     void* args[] = {&ra};
-    hipError_t e = hipLaunchKernel(v->fn, dim3(unsigned(grid)), dim3(unsigned(v->block)), args,
-                                   size_t(lds), static_cast<hipStream_t>(stream));
-    hipError_t e2 = hipGetLastError();
-    if (e == hipSuccess) e = e2;
+    const hipError_t e = hipLaunchKernel(v->fn, dim3(unsigned(grid)), dim3(unsigned(v->block)),
+                                         args, size_t(lds), static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(FNORM_ERR_LAUNCH, op, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -726,9 +753,10 @@ int fnorm_dual_head_rms_v(const void* q, const void* k, const void* qw, const vo
     if (q_rows < 0 || k_rows < 0)
         return fail(FNORM_ERR_SHAPE, op, "q_rows=%lld k_rows=%lld must be >= 0",
                     (long long)q_rows, (long long)k_rows);
-    // contiguous head vectors: one "token" whose heads are all the rows
-    return dual_impl(op, q, q_rows * head_dim, k, k_rows * head_dim, qw, kw, qy,
-                     q_rows * head_dim, ky, k_rows * head_dim, 1, q_rows, k_rows, head_dim, eps,
+    // contiguous head vectors: one "token" whose heads are all the rows (a
+    // single token's stride is never used, so none is formed: rows * head_dim
+    // is only computed after the size checks)
+    return dual_impl(op, q, 0, k, 0, qw, kw, qy, 0, ky, 0, 1, q_rows, k_rows, head_dim, eps,
                      dtype, stream, variant);
 }
 
@@ -754,10 +782,16 @@ int fnorm_dual_head_rms_rope_v(const void* q, const void* k, const void* qw, con
                                int64_t k_heads, int64_t head_dim, float eps, int64_t rope_dims,
                                int traditional, float base, float scale, int64_t offset,
                                const float* freqs, int dtype, void* stream, int variant) {
-    return rope_impl("fnorm_dual_head_rms_rope", q, q_heads * head_dim, k, k_heads * head_dim,
-                     qw, kw, qy, q_heads * head_dim, ky, k_heads * head_dim, tokens, q_heads,
-                     k_heads, head_dim, eps, rope_dims, traditional, base, scale, offset, freqs,
-                     dtype, stream, variant);
+    static const char* op = "fnorm_dual_head_rms_rope";
+    // token strides of the packed layout, formed only when they fit (negative
+    // counts are reported by the shared checks)
+    if (!product_fits(q_heads, head_dim) || !product_fits(k_heads, head_dim))
+        return fail(FNORM_ERR_SHAPE, op, "heads * head_dim overflows");
+    const int64_t qs = q_heads > 0 && head_dim > 0 ? q_heads * head_dim : 0;
+    const int64_t ks = k_heads > 0 && head_dim > 0 ? k_heads * head_dim : 0;
+    return rope_impl(op, q, qs, k, ks, qw, kw, qy, qs, ky, ks, tokens, q_heads, k_heads,
+                     head_dim, eps, rope_dims, traditional, base, scale, offset, freqs, dtype,
+                     stream, variant);
 }
 
 int fnorm_dual_head_rms_rope(const void* q, const void* k, const void* qw, const void* kw,
@@ -783,24 +817,83 @@ int fnorm_dual_head_rms_rope_strided(const void* q, int64_t q_stride, const void
 }
 
 int fnorm_variant_count(int op, int dtype, int64_t width, int aligned) {
-    if (!valid_dtype(dtype) || width <= 0 || op < 0 || op > 3) return 0;
+    if (!valid_dtype(dtype) || width <= 0 || !valid_op(op)) return 0;
     const Variant* list[kMaxCandidates];
     return 2 * candidates(op_kind(op, true), dtype, width, aligned != 0, list);
 }
 
-int fnorm_describe(int op, int dtype, int64_t width, int aligned, int variant, char* buf,
-                   int64_t len) {
-    static const char* name = "fnorm_describe";
+int fnorm_describe_shape(int op, int dtype, int64_t width, int aligned, int variant, char* buf,
+                         int64_t len) {
+    static const char* name = "fnorm_describe_shape";
     if (!buf || len <= 0) return fail(FNORM_ERR_NULL, name, "buf must be non-NULL, len > 0");
     buf[0] = '\0';
     if (!valid_dtype(dtype)) return fail(FNORM_ERR_DTYPE, name, "dtype %d", dtype);
     if (width <= 0) return fail(FNORM_ERR_SHAPE, name, "width %lld", (long long)width);
-    if (op < 0 || op > 3) return fail(FNORM_ERR_UNSUPPORTED, name, "op %d", op);
+    if (!valid_op(op)) return fail(FNORM_ERR_UNSUPPORTED, name, "op %d", op);
     Choice c;
     if (!pick(op_kind(op, true), dtype, width, aligned != 0, variant, &c))
         return fail(FNORM_ERR_UNSUPPORTED, name, "no variant %d", variant);
     describe_choice(c, buf, size_t(len));
     return ok();
+}
+
+// The kernel name of a planned call, "none" when the call launches nothing.
+static int describe_plan(int status, const Choice& c, char* buf, int64_t len) {
+    if (status != FNORM_OK) return status;
+    if (!c.v) std::snprintf(buf, size_t(len), "none");
+    else describe_choice(c, buf, size_t(len));
+    return ok();
+}
+
+int fnorm_describe(int op, const void* x, int64_t x_stride, const void* g, int64_t g_stride,
+                   const void* w, const void* b, const void* y, int64_t y_stride, int64_t rows,
+                   int64_t width, int dtype, int variant, char* buf, int64_t len) {
+    static const char* name = "fnorm_describe";
+    if (!buf || len <= 0) return fail(FNORM_ERR_NULL, name, "buf must be non-NULL, len > 0");
+    buf[0] = '\0';
+    if (op != FNORM_OP_RMS && op != FNORM_OP_LAYER && op != FNORM_OP_LAYER_NOBIAS &&
+        op != FNORM_OP_RMS_SWIGLU)
+        return fail(FNORM_ERR_UNSUPPORTED, name, "op %d is not a row operation", op);
+    const int fop = op == FNORM_OP_LAYER_NOBIAS ? FNORM_OP_LAYER : op;
+    const void* bias = op == FNORM_OP_LAYER ? b : nullptr;
+    const void* gate = op == FNORM_OP_RMS_SWIGLU ? g : nullptr;
+    Choice c;
+    const int s = rows_impl(name, fop, x, x_stride, gate, g_stride, w, bias, const_cast<void*>(y),
+                            y_stride, rows, width, 0.0f, dtype, nullptr, variant, &c);
+    return describe_plan(s, c, buf, len);
+}
+
+int fnorm_describe_dual(const void* q, int64_t q_stride, const void* k, int64_t k_stride,
+                        const void* qw, const void* kw, const void* qy, int64_t qy_stride,
+                        const void* ky, int64_t ky_stride, int64_t tokens, int64_t q_heads,
+                        int64_t k_heads, int64_t head_dim, int dtype, int variant, char* buf,
+                        int64_t len) {
+    static const char* name = "fnorm_describe_dual";
+    if (!buf || len <= 0) return fail(FNORM_ERR_NULL, name, "buf must be non-NULL, len > 0");
+    buf[0] = '\0';
+    Choice c;
+    const int s = dual_impl(name, q, q_stride, k, k_stride, qw, kw, const_cast<void*>(qy),
+                            qy_stride, const_cast<void*>(ky), ky_stride, tokens, q_heads, k_heads,
+                            head_dim, 0.0f, dtype, nullptr, variant, &c);
+    return describe_plan(s, c, buf, len);
+}
+
+int fnorm_describe_dual_rope(const void* q, int64_t q_stride, const void* k, int64_t k_stride,
+                             const void* qw, const void* kw, const void* qy, int64_t qy_stride,
+                             const void* ky, int64_t ky_stride, int64_t tokens, int64_t q_heads,
+                             int64_t k_heads, int64_t head_dim, int64_t rope_dims,
+                             int traditional, float base, float scale, int64_t offset,
+                             const float* freqs, int dtype, int variant, char* buf,
+                             int64_t len) {
+    static const char* name = "fnorm_describe_dual_rope";
+    if (!buf || len <= 0) return fail(FNORM_ERR_NULL, name, "buf must be non-NULL, len > 0");
+    buf[0] = '\0';
+    Choice c;
+    const int s = rope_impl(name, q, q_stride, k, k_stride, qw, kw, const_cast<void*>(qy),
+                            qy_stride, const_cast<void*>(ky), ky_stride, tokens, q_heads, k_heads,
+                            head_dim, 0.0f, rope_dims, traditional, base, scale, offset, freqs,
+                            dtype, nullptr, variant, &c);
+    return describe_plan(s, c, buf, len);
 }
 
 int fnorm_rope_variant_count(int dtype, int64_t head_dim, int64_t rope_dims, int traditional,
@@ -931,10 +1024,8 @@ int fnorm_bench_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     u32x4* d = static_cast<u32x4*>(dst);
     int64_t n = n16;
     void* args[] = {&s, &d, &n};
-    hipError_t e = hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(kBlock), args, 0,
-                                   static_cast<hipStream_t>(stream));
-    hipError_t e2 = hipGetLastError();
-    if (e == hipSuccess) e = e2;
+    const hipError_t e = hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(kBlock), args, 0,
+                                         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(FNORM_ERR_LAUNCH, op, "launch failed: %s", hipGetErrorString(e));
     return ok();
 }
