@@ -8,15 +8,17 @@ input, inputs resident in HBM:
   3. LayerNorm bf16 [65536, 4096] (mean 3, 0.1% outliers x100), with bias
 
 Metric: achieved HBM GB/s over the algorithmic bytes (read x once, write y
-once, read the weights/bias once per launch) and rows/s.  Timing: W warm-up
-steps (default 200, about 60 ms: per-kernel times drift down for the first
-tens of ms of sustained load), then K steps bracketed by synchronize and two
-HIP events on the stream the kernels run on (the step time and ``value``),
-then K more steps with an event after every launch (per-kernel durations and
-the roofline; those events add about 12 us to a step, so they are kept out
-of the first region).  The step order makes every input cold in the
-caches: 1.6 GB of other traffic separates two reads of the same tensor, more
-than the 256 MB MALL.
+once, read the weights/bias once per launch) and rows/s.  Timing: whole steps
+for at least 300 ms (the settle: per-kernel times drift down for the first
+tens of ms of sustained load), W warm-up steps, then K steps bracketed by
+synchronize and two HIP events on the stream the kernels run on (the step
+time and ``value``).  Per kernel (``per_op``, and the roofline): the kernel
+alone, launched back to back over input/output sets used in turn so every
+launch is cold, two events around the launches.  K more steps with an event
+after every launch give each kernel's time inside the step (``in_step``; the
+events add about 12 us to a step).  The step order makes every input cold in
+the caches: 1.6 GB of other traffic separates two reads of the same tensor,
+more than the 256 MB MALL.
 
 Prints ONE JSON line.  Extra legs (outside the timed region): the plain
 copy kernel over the LayerNorm's bytes (practical ceiling), fused against
@@ -68,9 +70,8 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=200,
-                   help="untimed steps; the GPU needs tens of ms of sustained load "
-                        "before its clocks settle")
+    p.add_argument("--warmup", type=int, default=20,
+                   help="untimed steps after the time-based settle")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-composed", action="store_true",
                    help="skip the fused-vs-composed ABBA comparison")
@@ -132,7 +133,19 @@ def main():
                      trn.describe(trn.OP_LAYER, trn.BF16, 4096)))
 
     stream = torch.cuda.current_stream(dev)
-    log(f"[bench] warmup {args.warmup} steps")
+    # Settle: whole steps for at least SETTLE_MS of sustained load before the
+    # warm-up steps, so that the timed region does not depend on --warmup
+    # (kernel times drift down over the first tens of ms of load)
+    log(f"[bench] settle >= {SETTLE_MS} ms, then warmup {args.warmup} steps")
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < SETTLE_MS:
+        for _ in range(10):
+            for _, fn, _, _, _ in plan:
+                fn()
+        torch.cuda.synchronize()
+        settle_steps += 10
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     for _ in range(args.warmup):
         for _, fn, _, _, _ in plan:
             fn()
@@ -178,12 +191,41 @@ def main():
         durs = sorted(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(K))
         avg = sum(durs) / K
         per_op[name] = {"kernel": kname, "bytes": b, "rows": rows,
-                        "avg_ms": round(avg, 5), "min_ms": round(durs[0], 5),
-                        "median_ms": round(durs[K // 2], 5),
-                        "gbs": round(b / (avg * 1e-3) / 1e9, 1),
-                        "frac_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                        "rows_per_s": round(rows / (avg * 1e-3), 1)}
-        log(f"[bench] {name}: {per_op[name]}")
+                        "in_step": {"avg_ms": round(avg, 5), "min_ms": round(durs[0], 5),
+                                    "median_ms": round(durs[K // 2], 5),
+                                    "gbs": round(b / (avg * 1e-3) / 1e9, 1),
+                                    "frac_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                    "note": "an event record after every kernel of the step; "
+                                            "includes part of the events' cost and the write-back "
+                                            "of lines the previous kernel left dirty"}}
+
+    # Each kernel alone: launches back to back on its own stream order, with
+    # enough input/output sets used in turn that every launch reads data the
+    # previous ones evicted from the 256 MB MALL and writes lines no earlier
+    # launch left dirty; two events around N launches give the average launch
+    # duration with no instrumentation between launches.  The roofline uses
+    # this figure.
+    for name, alone in standalone_arms(torch, trn, plan, dq, drms, dln, wl_dual, wl_rms,
+                                       wl_ln).items():
+        n_alone = max(K, 30)
+        for _ in range(2 * alone["sets"]):
+            alone["fn"]()
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(n_alone):
+            alone["fn"]()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        avg = a0.elapsed_time(a1) / n_alone
+        op = per_op[name]
+        op.update({"avg_ms": round(avg, 5), "launches": n_alone, "buffer_sets": alone["sets"],
+                   "gbs": round(op["bytes"] / (avg * 1e-3) / 1e9, 1),
+                   "frac_peak": round(op["bytes"] / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                   "rows_per_s": round(op["rows"] / (avg * 1e-3), 1)})
+        del alone
+        log(f"[bench] {name}: {op}")
+    torch.cuda.empty_cache()
     step_bytes = sum(p[2] for p in plan)
     step_rows = sum(p[3] for p in plan)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -247,7 +289,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(dom["bytes"] / (dom["avg_ms"] * 1e-3) / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(dom["bytes"] / (dom["avg_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                "traffic": traffic, "kernel": dominant}
+                "traffic": traffic, "kernel": dominant,
+                "duration": "average launch duration of the kernel alone (per_op)"}
 
     composed = None
     rope = None
@@ -290,14 +333,97 @@ def main():
                       "frac_peak_hbm": round(value / PEAK_HBM_GBS, 4),
                       "parallelism": "rows across workgroups (1 GPU)",
                       "layer_outliers": int(wl_ln.tensors["outliers"])},
-           "timing": {"value": f"{K} steps between two events on the launch stream",
-                      "per_op": f"{K} further steps with an event after every kernel",
+           "timing": {"value": f"{K} steps between two events on the launch stream, after "
+                               f"a {settle_ms:.0f} ms settle ({settle_steps} steps) and "
+                               f"{args.warmup} warm-up steps",
+                      "per_op": "each kernel alone: launches back to back over input/output "
+                                "sets used in turn (cold), two events around them",
+                      "per_op_in_step": f"{K} further steps with an event after every kernel",
+                      "settle_ms": round(settle_ms, 1), "settle_steps": settle_steps,
                       "ms_per_step_instrumented": round(ms_per_step_instrumented, 5)},
            "device": device, "per_op": per_op, "copy_ceiling": ceiling,
-           "roofline": roofline, "cpu_baseline": cpu, "fused_vs_composed": composed,
+           "roofline": roofline, "cpu_baseline": cpu,
+           "small_configs": small_configs(composed, inputs),
+           "fused_vs_composed": composed,
            "dual_rope": rope, "decode": decode, "rms_swiglu": gated,
            "wall_s_timed_region": round(wall, 4)}
     print(json.dumps(out), flush=True)
+
+
+SETTLE_MS = 300.0
+
+
+def standalone_arms(torch, trn, plan, dq, drms, dln, wl_dual, wl_rms, wl_ln):
+    """Per kernel of the step: a launch function that uses its own input/output
+    sets in turn, as many as make each launch's footprint, summed over the
+    sets, exceed 512 MiB (so no launch finds its rows in the MALL)."""
+    out = {}
+    names = [p[0] for p in plan]
+
+    def sets_for(nbytes):
+        return max(2, -(-(512 << 20) // nbytes) + 1)
+
+    for name in names:
+        if name.startswith("dual"):
+            n = sets_for(2 * (dq["q"].numel() + dq["k"].numel()) * 2)
+            sets = [(dq["q"].clone(), dq["k"].clone(), torch.empty_like(dq["q"]),
+                     torch.empty_like(dq["k"])) for _ in range(n)]
+            turn = [0]
+
+            def fn(sets=sets, turn=turn):
+                q, k, a, b = sets[turn[0]]
+                turn[0] = (turn[0] + 1) % len(sets)
+                trn.dual_head_rms_norm(q, k, dq["qw"], dq["kw"], wl_dual.eps, q_out=a, k_out=b)
+        elif name.startswith("rms"):
+            n = sets_for(2 * drms["x"].numel() * 2)
+            sets = [(drms["x"] if i == 0 else drms["x"].clone(), torch.empty_like(drms["x"]))
+                    for i in range(n)]
+            turn = [0]
+
+            def fn(sets=sets, turn=turn):
+                x, y = sets[turn[0]]
+                turn[0] = (turn[0] + 1) % len(sets)
+                trn.rms_norm(x, drms["w"], wl_rms.eps, out=y)
+        else:
+            n = sets_for(2 * dln["x"].numel() * 2)
+            sets = [(dln["x"] if i == 0 else dln["x"].clone(), torch.empty_like(dln["x"]))
+                    for i in range(n)]
+            turn = [0]
+
+            def fn(sets=sets, turn=turn):
+                x, y = sets[turn[0]]
+                turn[0] = (turn[0] + 1) % len(sets)
+                trn.layer_norm(x, dln["w"], dln["b"], wl_ln.eps, out=y)
+        out[name] = {"fn": fn, "sets": n}
+    return out
+
+
+def small_configs(composed, inputs):
+    """The two page-shaped workloads (the notebook's Part 1 RMSNorm input and
+    the kernel_micro_ab LayerNorm shape) in the metric's units, from the cold
+    arm of the fused-vs-composed leg: GB/s over the algorithmic bytes
+    (x in, y out, weights), rows/s and the fraction of 8 TB/s.  At 4-6 MB a
+    call is bound by its launch and ramp, not by HBM."""
+    if not composed:
+        return None
+    out = {}
+    for key, wl in (("rms_f32_4x128x1024_iota", inputs.rms_f32_512x1024("iota")),
+                    ("layer_f32_1x1024x768", inputs.layer_f32_1024x768())):
+        rec = composed.get(key, {}).get("cold")
+        if not rec:
+            continue
+        t = wl.tensors
+        nbytes = 2 * t["x"].numel() * 4 + t["w"].numel() * 4 + (
+            t["b"].numel() * 4 if "b" in t else 0)
+        rows = t["x"].numel() // t["x"].shape[-1]
+        us = rec["fused"]["min_us"]
+        out[key] = {"us_min": us, "us_mean": rec["fused"]["mean_us"], "bytes": nbytes,
+                    "rows": rows, "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                    "rows_per_s": round(rows / (us * 1e-6), 1),
+                    "frac_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                    "bound": "launch (4-6 MB per call)",
+                    "cache": "cold: a 512 MiB copy evicts the MALL before every timed call"}
+    return out
 
 
 def fused_vs_composed(trn, inputs, dev, stream, d, wl_rms, wl_ln, log):

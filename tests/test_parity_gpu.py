@@ -187,7 +187,9 @@ VARIANT_CASES = [("rms", torch.bfloat16, 128), ("rms", torch.bfloat16, 768),
                  ("rms", torch.float32, 180), ("layer", torch.bfloat16, 6144),
                  ("layer", torch.float32, 3000), ("layer", torch.bfloat16, 24576),
                  ("layer", torch.bfloat16, 192), ("rms", torch.float32, 96),
-                 ("layer", torch.bfloat16, 576), ("layer", torch.float32, 320)]
+                 ("layer", torch.bfloat16, 576), ("layer", torch.float32, 320),
+                 ("rms", torch.bfloat16, 576), ("rms", torch.bfloat16, 640),
+                 ("rms", torch.float32, 288), ("rms", torch.bfloat16, 192)]
 
 
 @pytest.mark.parametrize("op,dtype,width", VARIANT_CASES,
@@ -209,7 +211,7 @@ def test_every_variant(o, op, dtype, width):
         check(op, y, r, t, f"{op} w={width} variant {v}", kernel=name)
 
 
-@pytest.mark.parametrize("hd", [64, 80, 96, 128, 256, 100, 512, 1024])
+@pytest.mark.parametrize("hd", [64, 80, 96, 128, 192, 256, 100, 512, 576, 640, 1024])
 def test_dual_equals_two_singles(o, hd):
     for dtype in (torch.bfloat16, torch.float32, torch.float16):
         g = torch.Generator().manual_seed(hd)
@@ -274,13 +276,19 @@ def test_misaligned_pointers(o):
             ybig = torch.empty(50 * 1024 + 1, dtype=dtype, device=DEV)
             y = ybig[1:].view(50, 1024)
             if op == "rms":
+                name = trn.describe_call(trn.OP_RMS, x, w, out=y)
                 trn.rms_norm(x, w, 1e-5, out=y)
             else:
                 bbig = torch.empty(1025, dtype=dtype, device=DEV)
                 b = bbig[1:]
                 b.copy_(t["b"].to(DEV))
+                name = trn.describe_call(trn.OP_LAYER, x, w, b, out=y)
                 trn.layer_norm(x, w, b, 1e-5, out=y)
             torch.cuda.synchronize()
+            # the library's own answer for this call: the scalar-access kernel
+            assert ".vec1." in name, name
+            assert name == trn.describe(trn.OP_RMS if op == "rms" else trn.OP_LAYER, dcode(dtype),
+                                        1024, aligned=False)
             check(op, y.cpu(), run_oracle(o, op, t, 1e-5), t, f"misaligned {op}")
 
 
@@ -289,10 +297,16 @@ def test_in_place(o):
         for width in (128, 4096, 8192, 1000, 20000):
             t = inputs.random_rows(op, 20, width, torch.bfloat16, seed=width)
             x = t["x"].to(DEV).clone()
+            w, b = t["w"].to(DEV), t.get("b")
+            b = None if op == "rms" else b.to(DEV)
+            opc = trn.OP_RMS if op == "rms" else trn.OP_LAYER
+            # in place takes the kernel of the out-of-place call
+            assert trn.describe_call(opc, x, w, b, out=x) == trn.describe_call(
+                opc, x, w, b, out=torch.empty_like(x))
             if op == "rms":
-                trn.rms_norm(x, t["w"].to(DEV), 1e-5, out=x)
+                trn.rms_norm(x, w, 1e-5, out=x)
             else:
-                trn.layer_norm(x, t["w"].to(DEV), t["b"].to(DEV), 1e-5, out=x)
+                trn.layer_norm(x, w, b, 1e-5, out=x)
             torch.cuda.synchronize()
             check(op, x.cpu(), run_oracle(o, op, t, 1e-5), t, f"in place {op} {width}")
 

@@ -50,6 +50,8 @@ def run(op, x, w, b, eps, out=None, variant=-1):
     return trn.layer_norm(x, w, b, eps, out=out, variant=variant)
 
 
+DCODE = {torch.float32: trn.F32, torch.bfloat16: trn.BF16, torch.float16: trn.F16}
+
 STRIDE_CASES = [  # (op, width, x row stride, x column offset, y row stride, y column offset)
     ("rms", 128, 384, 128, 256, 64),        # heads of a packed buffer
     ("rms", 4096, 4096 + 64, 32, 4096, 0),  # padded rows into a packed output
@@ -77,6 +79,8 @@ def test_row_strided_matches_oracle_and_contiguous(o, case, dtype):
     x.copy_(t["x"].to(DEV))
     ybuf = torch.full((rows, ys), 7.0, dtype=dtype, device=DEV)
     y = ybuf[:, yc:yc + width]
+    opc = trn.OP_RMS if op == "rms" else trn.OP_LAYER
+    name = trn.describe_call(opc, x, w, b, out=y)
     got = run(op, x, w, b, 1e-5, out=y)
     assert got.data_ptr() == y.data_ptr()
     ref = run(op, t["x"].to(DEV), w, b, 1e-5)
@@ -85,8 +89,15 @@ def test_row_strided_matches_oracle_and_contiguous(o, case, dtype):
                       t["w"], t.get("b"), f"strided {op} {width}")
     aligned = (xs * eb) % 16 == 0 and (ys * eb) % 16 == 0 and (xc * eb) % 16 == 0 \
         and (yc * eb) % 16 == 0
+    # the library names the kernel this strided call took: the contiguous
+    # call's when every pointer and stride is 16-byte aligned, else the
+    # scalar-access kernel
+    contiguous = trn.describe_call(opc, t["x"].to(DEV), w, b)
     if aligned:   # the same kernel as the contiguous call
+        assert name == contiguous, (name, contiguous)
         assert torch.equal(bits(y), bits(ref))
+    else:
+        assert ".vec1." in name and name == trn.describe(opc, DCODE[dtype], width, aligned=False)
     # the bytes around the rows are untouched
     mask = torch.ones(rows, ys, dtype=torch.bool)
     mask[:, yc:yc + width] = False
@@ -137,7 +148,6 @@ def test_row_strided_in_place(o):
         assert torch.equal(bits(buf[1::2]), bits(before_odd))
 
 
-DCODE = {torch.float32: trn.F32, torch.bfloat16: trn.BF16, torch.float16: trn.F16}
 
 
 def fresh(t):
@@ -175,6 +185,14 @@ def test_packed_qkv_dual_in_place(o, case):
     buf, q, k, v, qw, kw = packed_qkv(tokens, qh, kh, hd, dtype, seed=tokens + hd)
     q0, k0, v0 = fresh(q), fresh(k), fresh(v)
     ref_q, ref_k = trn.dual_head_rms_norm(q0, k0, qw, kw, 1e-6)
+    # packed views whose token stride is a 16-byte multiple take the
+    # contiguous call's kernel
+    name = trn.describe_dual_call(q, k, qw, kw, q_out=q, k_out=k)
+    eb = torch.finfo(dtype).bits // 8
+    if (q.stride(0) * eb) % 16 == 0 and (qh * hd * eb) % 16 == 0 and (hd * eb) % 16 == 0:
+        assert name == trn.describe_dual_call(q0, k0, qw, kw), name
+    else:
+        assert ".vec1." in name, name
     yq, yk = trn.dual_head_rms_norm(q, k, qw, kw, 1e-6, q_out=q, k_out=k)
     torch.cuda.synchronize()
     assert yq.data_ptr() == q.data_ptr() and yk.data_ptr() == k.data_ptr()

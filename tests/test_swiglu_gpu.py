@@ -57,7 +57,8 @@ def case(rows, width, dtype, seed, extremes=True):
     return t
 
 
-WIDTHS = [1, 3, 8, 64, 100, 128, 256, 768, 1024, 2560, 4096, 5120, 8192, 20000]
+WIDTHS = [1, 3, 8, 64, 100, 128, 192, 256, 576, 640, 768, 1024, 2560, 4096, 5120, 8192,
+          20000]
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: str(d)[6:])

@@ -24,9 +24,10 @@
 #include "fnorm_table.hpp"
 
 namespace fnorm {
+
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0: strided forms, fused RoPE, gated RMSNorm
+constexpr int kVersion = 201;  // 0.2.1: call-level describe
 
 thread_local char g_err[512];
 

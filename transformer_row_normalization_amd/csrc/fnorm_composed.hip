@@ -18,6 +18,9 @@
 // correctly rounded (HIP's default for fp32).
 #include <hip/hip_runtime.h>
 
+#include <tuple>
+#include <utility>
+
 #include "fnorm_composed.hpp"
 #include "fnorm_device.hpp"
 
@@ -119,11 +122,19 @@ struct Launch {
     int grid_scalar;    // workgroups for per-row scalar kernels
     hipError_t err = hipSuccess;
 
-    template <typename K, typename... A>
-    void go(K kernel, int grid, A... args) {
+    // The launch's own status (the thread's last-error slot may hold an
+    // earlier, unrelated failure).  The arguments are converted to the
+    // kernel's parameter types before their addresses are passed.
+    template <typename... P, typename... A>
+    void go(void (*kernel)(P...), int grid, A... args) {
         if (err != hipSuccess) return;
-        hipLaunchKernelGGL(kernel, dim3(unsigned(grid)), dim3(kBlock), 0, stream, args...);
-        err = hipGetLastError();
+        launch(kernel, grid, std::tuple<P...>(args...), std::index_sequence_for<P...>{});
+    }
+    template <typename... P, size_t... I>
+    void launch(void (*kernel)(P...), int grid, std::tuple<P...> t, std::index_sequence<I...>) {
+        void* pa[] = {static_cast<void*>(&std::get<I>(t))...};
+        err = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(unsigned(grid)),
+                              dim3(kBlock), pa, 0, stream);
     }
 };
 
