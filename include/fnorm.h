@@ -295,6 +295,24 @@ int fnorm_layer_composed(const void* x, const void* w, const void* b, void* y, i
                          int64_t width, float eps, int dtype, void* workspace,
                          int64_t workspace_bytes, void* stream);
 
+/*
+ * The composed RMSNorm (as fnorm_rms_composed) for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It takes no workspace and calls no allocating routine:
+ * its fp32 intermediates live in a static device buffer of the library, 32
+ * MiB per device (held by each device the library runs on until the process
+ * ends), which serves rows * width up to about 8.38 million elements
+ * (fnorm_composed_workspace_bytes(FNORM_OP_RMS, rows, width) <= 33554432);
+ * larger calls return FNORM_ERR_WORKSPACE before any HIP call.  Every call
+ * on one device shares that buffer: calls that overlap in time on one device
+ * (two streams, or two threads) race and must be serialized by the caller.
+ * The buffer keeps the last call's contents; the chain writes every
+ * intermediate before reading it, so nothing needs clearing.  Results are
+ * bitwise those of fnorm_rms_composed.  Other conventions as above.
+ */
+int fnorm_rms_composed_noalloc(const void* x, const void* w, void* y, int64_t rows,
+                               int64_t width, float eps, int dtype, void* stream);
+
 /* Variant count and kernel name of the fused dual norm + RoPE, as above. */
 int fnorm_rope_variant_count(int dtype, int64_t head_dim, int64_t rope_dims, int traditional,
                              int aligned);

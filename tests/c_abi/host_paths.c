@@ -207,6 +207,14 @@ static void entry_points(void)
            FNORM_ERR_SHAPE);
     EXPECT("composed ws", fnorm_layer_composed(A, B, NULL, C, 4, 8, 1e-6f, FNORM_F32, D, 3, NULL),
            FNORM_ERR_WORKSPACE);
+    /* beyond the static scratch: refused before any HIP call */
+    EXPECT("noalloc size", fnorm_rms_composed_noalloc(A, B, C, 4096, 4096, 1e-6f, FNORM_F32, NULL),
+           FNORM_ERR_WORKSPACE);
+    EXPECT("noalloc rows", fnorm_rms_composed_noalloc(A, B, C, -1, 8, 1e-6f, FNORM_F32, NULL),
+           FNORM_ERR_SHAPE);
+    EXPECT("noalloc none", fnorm_rms_composed_noalloc(NULL, NULL, NULL, 0, 8, 1e-6f, FNORM_F32,
+                                                      NULL),
+           FNORM_OK);
     EXPECT("copy alias", fnorm_bench_copy(A, A + 16, 64, NULL), FNORM_ERR_ALIAS);
     CHECK(fnorm_composed_workspace_bytes(0, INT64_MAX / 2, 1 << 20) == -1);
     CHECK(strlen(fnorm_last_error()) != 0);

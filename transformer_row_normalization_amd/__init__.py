@@ -86,6 +86,7 @@ _SIGNATURES = {
     "fnorm_rms_swiglu_strided": ([_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I64, _F, _I, _P, _I],
                                  _I),
     "fnorm_rms_composed": ([_P, _P, _P, _I64, _I64, _F, _I, _P, _I64, _P], _I),
+    "fnorm_rms_composed_noalloc": ([_P, _P, _P, _I64, _I64, _F, _I, _P], _I),
     "fnorm_layer_composed": ([_P, _P, _P, _P, _I64, _I64, _F, _I, _P, _I64, _P], _I),
 }
 
@@ -343,6 +344,21 @@ def rms_norm_composed(x, w, eps: float = 1e-6, out=None, workspace=None):
     ws = composed_workspace(OP_RMS, x) if workspace is None else workspace
     _check(lib().fnorm_rms_composed(_ptr(x), _ptr(w), _ptr(y), x.numel() // width, width, eps,
                                     code, _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
+    return y
+
+
+def rms_norm_composed_noalloc(x, w, eps: float = 1e-6, out=None):
+    """The composed RMSNorm with its intermediates in the library's static
+    device scratch (no allocation; calls on one device must not overlap)."""
+    _require(x, "x", x.dtype, x.device)
+    _require(w, "w", x.dtype, x.device)
+    width = x.shape[-1]
+    if tuple(w.shape) != (width,):
+        raise ValueError(f"w has shape {tuple(w.shape)}, expected ({width},)")
+    y = _torch().empty_like(x) if out is None else out
+    _require(y, "out", x.dtype, x.device)
+    _check(lib().fnorm_rms_composed_noalloc(_ptr(x), _ptr(w), _ptr(y), x.numel() // width, width,
+                                            eps, _dtype_code(x), _stream(x)))
     return y
 
 

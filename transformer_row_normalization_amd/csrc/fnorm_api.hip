@@ -25,9 +25,17 @@
 
 namespace fnorm {
 
+// Scratch of fnorm_rms_composed_noalloc: the fp32 intermediates of the
+// composed chain, in device memory that belongs to the code object (each
+// device holds its own copy from module load to process exit), so the call
+// allocates nothing.  Host code never uses the name below as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr int64_t kNoAllocScratchBytes = int64_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 namespace {
 
-constexpr int kVersion = 201;  // 0.2.1: call-level describe
+constexpr int kVersion = 201;  // 0.2.1: call-level describe, no-alloc composed RMSNorm
 
 thread_local char g_err[512];
 
@@ -43,6 +51,35 @@ int fail(int status, const char* op, const char* fmt, ...) {
 
 int ok() {
     g_err[0] = '\0';
+    return FNORM_OK;
+}
+
+// Device address of `scratch` on the current device, looked up on the first
+// call there (with that device current) and kept per device.
+int noalloc_scratch(const char* op, void** out) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void*> addr[kMaxDevices];
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(FNORM_ERR_LAUNCH, op, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(FNORM_ERR_UNSUPPORTED, op, "device %d beyond the %d this call serves", dev,
+                    kMaxDevices);
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(mu);
+        p = addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p)
+                return fail(FNORM_ERR_LAUNCH, op, "hipGetSymbolAddress(scratch) failed: %s",
+                            hipGetErrorString(e));
+            addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
     return FNORM_OK;
 }
 
@@ -979,6 +1016,24 @@ int fnorm_rms_composed(const void* x, const void* w, void* y, int64_t rows, int6
                        void* stream) {
     return run_composed("fnorm_rms_composed", false, x, w, nullptr, y, rows, width, eps, dtype,
                         workspace, workspace_bytes, stream);
+}
+
+int fnorm_rms_composed_noalloc(const void* x, const void* w, void* y, int64_t rows,
+                               int64_t width, float eps, int dtype, void* stream) {
+    static const char* op = "fnorm_rms_composed_noalloc";
+    if (int s = check_scalars(op, dtype, rows, width, eps)) return s;
+    if (rows == 0) return ok();
+    const int64_t need = composed::workspace_bytes(false, rows, width);
+    if (need > kNoAllocScratchBytes)
+        return fail(FNORM_ERR_WORKSPACE, op,
+                    "rows=%lld width=%lld need %lld bytes of fp32 intermediates; the static "
+                    "scratch holds %lld (rows * width up to about %lld elements)",
+                    (long long)rows, (long long)width, (long long)need,
+                    (long long)kNoAllocScratchBytes, (long long)(kNoAllocScratchBytes / 4 - 4096));
+    void* ws = nullptr;
+    if (int s = noalloc_scratch(op, &ws)) return s;
+    return run_composed(op, false, x, w, nullptr, y, rows, width, eps, dtype, ws,
+                        kNoAllocScratchBytes, stream);
 }
 
 int fnorm_layer_composed(const void* x, const void* w, const void* b, void* y, int64_t rows,
