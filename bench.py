@@ -218,12 +218,23 @@ def main():
         a1.record(stream)
         torch.cuda.synchronize()
         avg = a0.elapsed_time(a1) / n_alone
+        if ":" in name:   # an alternative policy of a step kernel, reported beside it
+            base, tag = name.split(":")
+            op = per_op[base]
+            op[f"alone_{tag}_stores"] = {
+                "kernel": alone["kernel"], "avg_ms": round(avg, 5),
+                "gbs": round(op["bytes"] / (avg * 1e-3) / 1e9, 1),
+                "frac_peak": round(op["bytes"] / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "note": "not the default: inside the step this policy made the step slower "
+                        "(ordinary stores leave the output in the MALL and their write-back "
+                        "overlaps the next kernel)"}
+            log(f"[bench] {name}: {op[f'alone_{tag}_stores']}")
+            continue
         op = per_op[name]
         op.update({"avg_ms": round(avg, 5), "launches": n_alone, "buffer_sets": alone["sets"],
                    "gbs": round(op["bytes"] / (avg * 1e-3) / 1e9, 1),
                    "frac_peak": round(op["bytes"] / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                    "rows_per_s": round(op["rows"] / (avg * 1e-3), 1)})
-        del alone
         log(f"[bench] {name}: {op}")
     torch.cuda.empty_cache()
     step_bytes = sum(p[2] for p in plan)
@@ -380,10 +391,25 @@ def standalone_arms(torch, trn, plan, dq, drms, dln, wl_dual, wl_rms, wl_ln):
                     for i in range(n)]
             turn = [0]
 
-            def fn(sets=sets, turn=turn):
+            def fn(sets=sets, turn=turn, variant=-1):
                 x, y = sets[turn[0]]
                 turn[0] = (turn[0] + 1) % len(sets)
-                trn.rms_norm(x, drms["w"], wl_rms.eps, out=y)
+                trn.rms_norm(x, drms["w"], wl_rms.eps, out=y, variant=variant)
+
+            # the same shape with non-temporal stores, when the default keeps
+            # ordinary ones (the store policy is a trade-off: an ordinary
+            # store leaves the output in the MALL for its consumer, and its
+            # write-back overlaps the next kernel; alone, non-temporal stores
+            # are faster)
+            width = drms["x"].shape[-1]
+            default = trn.describe(trn.OP_RMS, trn.BF16, width)
+            if ".ntld." in default:
+                want = default.replace(".ntld.", ".nt.")
+                for v in range(trn.variant_count(trn.OP_RMS, trn.BF16, width)):
+                    if trn.describe(trn.OP_RMS, trn.BF16, width, variant=v) == want:
+                        out[name + ":nt"] = {"fn": (lambda f=fn, vv=v: f(variant=vv)), "sets": n,
+                                             "kernel": want}
+                        break
         else:
             n = sets_for(2 * dln["x"].numel() * 2)
             sets = [(dln["x"] if i == 0 else dln["x"].clone(), torch.empty_like(dln["x"]))
@@ -395,7 +421,7 @@ def standalone_arms(torch, trn, plan, dq, drms, dln, wl_dual, wl_rms, wl_ln):
                 turn[0] = (turn[0] + 1) % len(sets)
                 trn.layer_norm(x, dln["w"], dln["b"], wl_ln.eps, out=y)
         out[name] = {"fn": fn, "sets": n}
-    return out
+    return {k: out[k] for k in sorted(out, key=lambda k: (k.split(":")[0] not in names, k))}
 
 
 def small_configs(composed, inputs):
