@@ -7,6 +7,7 @@ Each strided result is checked against the fp64 oracle on the same rows
 point, which runs the same kernel; the bytes between rows must be left as
 they were.
 """
+import re
 import sys
 
 import numpy as np
@@ -244,3 +245,63 @@ def test_packed_qkv_to_separate_outputs(o):
     for a, b_ in ((yq, ref_q), (yk, ref_k), (oq, ref_q), (ok, ref_k)):
         assert torch.equal(bits(a), bits(b_))
     assert torch.all(out[:, (qh + kh) * hd:].cpu() == 0)
+
+
+def _variant_named(opc, code, width, aligned, name):
+    for v in range(trn.variant_count(opc, code, width, aligned)):
+        if trn.describe(opc, code, width, aligned, v) == name:
+            return v
+    raise AssertionError(f"no variant named {name}")
+
+
+@pytest.mark.parametrize("case", ["aligned", "misaligned", "odd_stride", "in_place", "no_bias"])
+def test_describe_call_names_the_kernel_that_runs(case):
+    """describe_call's answer is the kernel the call launches: forcing the
+    variant of that name gives bitwise the default call's output, and the
+    widths here are served by shapes with different reduction trees."""
+    dtype, rows, width = torch.bfloat16, 96, 4096
+    code = trn.BF16
+    t = inputs.random_rows("layer", rows, width, dtype, seed=17, mean=1.0, std=2.0)
+    w, b = t["w"].to(DEV), t["b"].to(DEV)
+    if case == "misaligned":
+        xbuf = torch.empty(rows * width + 1, dtype=dtype, device=DEV)
+        x = xbuf[1:].view(rows, width)
+        x.copy_(t["x"].to(DEV))
+    elif case == "odd_stride":
+        xbuf = torch.empty(rows, width + 3, dtype=dtype, device=DEV)
+        x = xbuf[:, :width]
+        x.copy_(t["x"].to(DEV))
+    else:
+        x = t["x"].to(DEV).clone()
+    if case == "no_bias":
+        b = None
+    aligned = case not in ("misaligned", "odd_stride")
+    opc = trn.OP_LAYER if b is not None else trn.OP_LAYER_NOBIAS
+    out = x if case == "in_place" else torch.empty(rows, width, dtype=dtype, device=DEV)
+    name = trn.describe_call(trn.OP_LAYER, x, w, b, out=out)
+    assert (".vec1." in name) == (not aligned), name
+    v = _variant_named(opc, code, width, aligned, name)
+    say(f"[describe] {case}: {name} (variant {v})")
+    x0 = x.clone()
+    y_default = trn.layer_norm(x, w, b, 1e-5, out=out).clone()
+    if case == "in_place":
+        x.copy_(x0)
+    y_forced = trn.layer_norm(x, w, b, 1e-5, out=out, variant=v)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(y_default), bits(y_forced))
+    if not aligned:
+        # the scalar-access shapes for this width (one element per access, 4
+        # per thread, 1024 lanes; and the wide kernel, 1024 threads striding by
+        # 1024) add the same elements in the same order: nothing to tell apart
+        return
+    # a kernel with another reduction tree (packs per lane, lanes per row)
+    # for the same width computes in a different order
+    def tree(n):
+        return tuple(re.findall(r"(?<=\.)(vec\d+|vpt\d+|lpr\d+|wide)(?=\.)", n))
+    other = next(u for u in range(trn.variant_count(opc, code, width, aligned))
+                 if tree(trn.describe(opc, code, width, aligned, u)) != tree(name))
+    if case == "in_place":
+        x.copy_(x0)
+    y_other = trn.layer_norm(x, w, b, 1e-5, out=out, variant=other)
+    torch.cuda.synchronize()
+    assert not torch.equal(bits(y_default), bits(y_other)), "shapes not distinguishable here"
