@@ -525,13 +525,48 @@ def fused_vs_composed(trn, inputs, dev, stream, d, wl_rms, wl_ln, log):
     return out
 
 
+def _abba_back_to_back(torch, stream, arms, reps=12, calls=20):
+    """Median and minimum per-launch time (us) of each arm: `calls` launches
+    back to back between two events on the stream, arms in ABBA order over
+    `reps` repetitions."""
+    for f in arms.values():
+        for _ in range(calls):
+            f()
+    torch.cuda.synchronize()
+    times = {k: [] for k in arms}
+    for r in range(reps):
+        for k in (list(arms) if r % 2 == 0 else list(arms)[::-1]):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(calls):
+                arms[k]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[k].append(e0.elapsed_time(e1) * 1e3 / calls)
+    out = {}
+    for k, v in times.items():
+        v = sorted(v)
+        out[k] = {"median_us": round((v[(reps - 1) // 2] + v[reps // 2]) / 2, 2),
+                  "min_us": round(v[0], 2)}
+    return out
+
+
+def _rotating(calls):
+    turn = [0]
+
+    def fn():
+        calls[turn[0]]()
+        turn[0] = (turn[0] + 1) % len(calls)
+    return fn
+
+
 def dual_rope_leg(trn, dq, qy, ky, eps, stream, log):
     """The dual workload with the rotary embedding fused into the same launch
     (positions 0..4095, base 10000, split-half) against the plain dual norm
     and the copy kernel over the same bytes.  Cold: 8 copies of the inputs
     (672 MB) are used in turn, so no call finds its rows in the 256 MB MALL.
-    ABBA over 12 reps of 20 back-to-back calls, an event pair around each
-    call; the rotation adds no HBM traffic."""
+    Each set's call is prepared once; 20 launches back to back between two
+    events, ABBA over 12 reps, medians.  The rotation adds no HBM traffic."""
     import torch
 
     sets = [(dq["q"].clone(), dq["k"].clone(), torch.empty_like(qy), torch.empty_like(ky))
@@ -539,50 +574,22 @@ def dual_rope_leg(trn, dq, qy, ky, eps, stream, log):
     flat = [(torch.cat([q.reshape(-1), k.reshape(-1)]),
              torch.empty(q.numel() + k.numel(), dtype=q.dtype, device=q.device))
             for q, k, _, _ in sets]
-    turn = [0]
-
-    def nxt():
-        turn[0] = (turn[0] + 1) % len(sets)
-        return turn[0]
-
-    def dual():
-        q, k, a, b = sets[nxt()]
-        trn.dual_head_rms_norm(q, k, dq["qw"], dq["kw"], eps, q_out=a, k_out=b)
-
-    def rope():
-        q, k, a, b = sets[nxt()]
-        trn.dual_head_rms_rope(q, k, dq["qw"], dq["kw"], eps, q_out=a, k_out=b)
-
-    def copy():
-        a, b = flat[nxt()]
-        trn.bench_copy(a, b)
-
-    arms = {"dual": dual, "dual_rope": rope, "copy": copy}
-    for f in arms.values():
-        for _ in range(len(sets)):
-            f()
-    torch.cuda.synchronize()
-    times = {k: [] for k in arms}
-    for r in range(12):
-        order = list(arms) if r % 2 == 0 else list(arms)[::-1]
-        for k in order:
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(20)]
-            for e0, e1 in evs:
-                e0.record(stream)
-                arms[k]()
-                e1.record(stream)
-            torch.cuda.synchronize()
-            times[k] += [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
+    arms = {
+        "dual": _rotating([trn.prepare(trn.dual_head_rms_norm, q, k, dq["qw"], dq["kw"], eps,
+                                       q_out=a, k_out=b)[0] for q, k, a, b in sets]),
+        "dual_rope": _rotating([trn.prepare(trn.dual_head_rms_rope, q, k, dq["qw"], dq["kw"],
+                                            eps, q_out=a, k_out=b)[0] for q, k, a, b in sets]),
+        "copy": _rotating([(lambda s_=s_, d_=d_: trn.bench_copy(s_, d_)) for s_, d_ in flat])}
+    out = _abba_back_to_back(torch, stream, arms)
     nbytes = 2 * (dq["q"].numel() + dq["k"].numel()) * 2
-    out = {}
-    for k, v in times.items():
-        v = sorted(v)
-        med = v[len(v) // 2]
-        out[k] = {"min_us": round(v[0], 2), "median_us": round(med, 2),
-                  "gbs_median": round(nbytes / (med * 1e-6) / 1e9, 1)}
+    for k, rec in out.items():
+        gbs = nbytes / (rec["median_us"] * 1e-6) / 1e9
+        rec.update({"gbs_median": round(gbs, 1), "frac_peak": round(gbs / PEAK_HBM_GBS, 4)})
+    out["dual_rope"]["frac_copy"] = round(out["copy"]["median_us"] /
+                                          out["dual_rope"]["median_us"], 4)
     out["kernel"] = trn.describe_rope(trn.BF16, 128, 128, False)
-    out["cache"] = "cold: 8 input copies used in turn"
+    out["bytes"] = nbytes
+    out["cache"] = "cold: 8 input copies used in turn; prepared calls back to back"
     del sets, flat
     log(f"[bench] dual + rope: {out}")
     return out
@@ -591,40 +598,42 @@ def dual_rope_leg(trn, dq, qy, ky, eps, stream, log):
 def gated_leg(trn, inputs, dev, stream, log):
     """RMSNorm with the SiLU-gate epilogue at the gated-delta output-norm
     shape (4096 tokens x 32 heads x 128, bf16) against the plain RMSNorm of
-    the same x: timed alone and cold (a 512 MiB fill before each call, so
-    that neither arm reads from the MALL), ABBA over 30 reps.  The fused
+    the same x and the copy kernel over each one's bytes: 8 input copies used
+    in turn (cold), prepared calls, 20
+    launches back to back between two events, ABBA over 12 reps.  The fused
     epilogue adds the gate read (6 bytes per element against 4); run as a
     separate pass it would re-read y and the gate and write y again."""
     import torch
 
     wl = inputs.rms_swiglu_bf16_4096tok()
-    x, g, w = (wl.tensors[k].to(dev) for k in ("x", "g", "w"))
-    y = torch.empty_like(x)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    arms = {"rms": lambda: trn.rms_norm(x, w, wl.eps, out=y),
-            "rms_swiglu": lambda: trn.rms_norm_swiglu(x, g, w, wl.eps, out=y)}
-    nbytes = {"rms": 2 * x.numel() * 2, "rms_swiglu": 3 * x.numel() * 2}
-    for f in arms.values():
-        f()
-    torch.cuda.synchronize()
-    times = {k: [] for k in arms}
-    for r in range(30):
-        for k in (list(arms) if r % 2 == 0 else list(arms)[::-1]):
-            flush.fill_(r & 255)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            arms[k]()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times[k].append(e0.elapsed_time(e1) * 1e3)
-    out = {}
-    for k, v in times.items():
-        v = sorted(v)
-        out[k] = {"min_us": round(v[0], 2), "median_us": round(v[len(v) // 2], 2),
-                  "bytes": nbytes[k], "gbs_median": round(nbytes[k] / (v[len(v) // 2] * 1e-6) / 1e9, 1)}
+    x0, g0, w = (wl.tensors[k].to(dev) for k in ("x", "g", "w"))
+    sets = [(x0.clone(), g0.clone(), torch.empty_like(x0)) for _ in range(8)]
+    n = x0.numel()
+    # the copy kernel over the same total bytes: n elements in and out for the
+    # plain norm, 1.5 n for the gated one (x and g in, y out)
+    flat = {m: [(torch.empty(m, dtype=x0.dtype, device=dev), torch.empty(m, dtype=x0.dtype, device=dev))
+                for _ in range(8)] for m in (n, 3 * n // 2)}
+    arms = {"rms": _rotating([trn.prepare(trn.rms_norm, x, w, wl.eps, out=y)[0]
+                              for x, _, y in sets]),
+            "rms_swiglu": _rotating([trn.prepare(trn.rms_norm_swiglu, x, g, w, wl.eps, out=y)[0]
+                                     for x, g, y in sets]),
+            "copy_rms_bytes": _rotating([(lambda s_=s_, d_=d_: trn.bench_copy(s_, d_))
+                                         for s_, d_ in flat[n]]),
+            "copy_rms_swiglu_bytes": _rotating([(lambda s_=s_, d_=d_: trn.bench_copy(s_, d_))
+                                                for s_, d_ in flat[3 * n // 2]])}
+    nbytes = {"rms": 2 * n * 2, "rms_swiglu": 3 * n * 2, "copy_rms_bytes": 2 * n * 2,
+              "copy_rms_swiglu_bytes": 3 * n * 2}
+    out = _abba_back_to_back(torch, stream, arms)
+    for k, rec in out.items():
+        gbs = nbytes[k] / (rec["median_us"] * 1e-6) / 1e9
+        rec.update({"bytes": nbytes[k], "gbs_median": round(gbs, 1),
+                    "frac_peak": round(gbs / PEAK_HBM_GBS, 4)})
+    for k in ("rms", "rms_swiglu"):
+        out[k]["frac_copy"] = round(out[f"copy_{k}_bytes"]["median_us"] / out[k]["median_us"], 4)
     out["shape"] = "x, g [4096, 32, 128] bf16 (131072 rows of 128)"
     out["kernel"] = trn.describe(trn.OP_RMS_SWIGLU, trn.BF16, 128)
-    del flush
+    out["cache"] = "cold: 8 input copies used in turn; prepared calls back to back"
+    del sets, flat
     log(f"[bench] gated output norm: {out}")
     return out
 
