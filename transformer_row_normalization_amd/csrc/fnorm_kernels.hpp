@@ -510,12 +510,6 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
     float2* wtab = cs + int64_t(wave) * W * half;
     const int ihalf = static_cast<int>(half);
 
-    // Lane L computes the table entries of pairs L + 64 j; the inverse
-    // frequencies of its first two are fetched once, before any row load, so
-    // that waiting for them never waits for a row.
-    const double inv0 = wave_lane < ihalf ? inv_turns(wave_lane) : 0.0;
-    const double inv1 = wave_lane + 64 < ihalf ? inv_turns(wave_lane + 64) : 0.0;
-
     R wv[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
@@ -548,28 +542,28 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
         const int leader = first > wave_row0 ? int(first - wave_row0) : 0;
         const double pos = static_cast<double>(ra.offset + tok) * static_cast<double>(ra.scale);
 
-        // Angle table of the wavefront's leader slots, one leader at a time:
-        // lane L writes pairs L, L + 64, ... of the leader's token.
+        // Angle table of the wavefront's leader slots: leader k's pair i is
+        // work item k * half + i, spread round-robin over the 64 lanes.
         uint64_t leaders = __ballot(lane == 0 && leader == wslot);
+        int k = 0;
         while (leaders) {                                   // uniform over the wave
             const int bit = __builtin_ctzll(leaders);
             leaders &= leaders - 1;
+            const int g = bit / LPR;
             const int64_t pb = __builtin_bit_cast(int64_t, pos);
             const int lo = __builtin_amdgcn_readlane(int(pb & 0xffffffff), bit);
             const int hi = __builtin_amdgcn_readlane(int(pb >> 32), bit);
             const double pg = __builtin_bit_cast(double, (int64_t(hi) << 32) | uint32_t(lo));
-            float2* const row_tab = wtab + (bit / LPR) * ihalf;
-            // theta / (2 pi) in fp64, reduced to a fraction of a turn
-            // exactly (t - rint(t)); the hardware sine and cosine take
-            // their argument in turns (v_sin_f32 / v_cos_f32)
-            auto put = [&](int i, double inv) {
-                const double t = pg * inv;
+            for (int i = (wave_lane - (k * ihalf) % 64 + 64) % 64; i < ihalf; i += 64) {
+                // theta / (2 pi) in fp64, reduced to a fraction of a turn
+                // exactly (t - rint(t)); the hardware sine and cosine take
+                // their argument in turns (v_sin_f32 / v_cos_f32)
+                const double t = pg * inv_turns(i);
                 const float f = static_cast<float>(t - __builtin_rint(t));
-                row_tab[i] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
-            };
-            if (wave_lane < ihalf) put(wave_lane, inv0);
-            if (wave_lane + 64 < ihalf) put(wave_lane + 64, inv1);
-            for (int i = wave_lane + 128; i < ihalf; i += 64) put(i, inv_turns(i));
+                wtab[g * ihalf + i] =
+                    make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+            }
+            ++k;
         }
         // The table is written and read by this wavefront only, and a
         // wavefront's LDS operations execute in order: wavefront-scope
