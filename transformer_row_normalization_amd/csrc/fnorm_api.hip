@@ -21,6 +21,7 @@
 #include "../../include/fnorm.h"
 #include "fnorm_composed.hpp"
 #include "fnorm_kernels.hpp"
+#include "fnorm_rope.hpp"
 #include "fnorm_table.hpp"
 
 namespace fnorm {

@@ -1,6 +1,7 @@
 // Kernel instances of the fused dual head RMSNorm + RoPE (head-vector
 // shapes: one row per lane group of at most one wavefront).
 #include "fnorm_kernels.hpp"
+#include "fnorm_rope.hpp"
 #include "fnorm_table.hpp"
 
 namespace fnorm {
