@@ -551,6 +551,13 @@ ROPE_CASES = [  # (dtype, tokens, q_heads, k_heads, head_dim, dims, traditional,
     # then chosen at run time): half the features of head_dim 256 and 512
     (torch.bfloat16, 29, 6, 2, 256, 128, False, 10000.0, 1.0, 31, False),
     (torch.bfloat16, 13, 4, 1, 512, 256, False, 500000.0, 1.0, 8, False),
+    # split-half rows wider than 128 features fetch a lane's first two
+    # frequencies before the row loop: full rotation past 128 pairs, a
+    # caller's table, and partial rotation with a second entry on half the lanes
+    (torch.bfloat16, 11, 4, 2, 512, 512, False, 10000.0, 1.0, 65537, False),
+    (torch.bfloat16, 21, 4, 2, 256, 256, False, 10000.0, 1.0, 99, True),
+    (torch.bfloat16, 15, 5, 3, 256, 192, False, 10000.0, 1.0, 4096, False),
+    (torch.float32, 9, 3, 2, 256, 192, False, 10000.0, 1.0, 123, True),
 ]
 
 

@@ -113,14 +113,16 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
     float2* wtab = cs + int64_t(wave) * W * half;
     const int ihalf = static_cast<int>(half);
 
-    // Split-half rows of more than 128 features give a lane two or more
-    // table entries per token.  In those kernels a lane's pairs are fixed
-    // (L, L + 64, ...) and the inverse frequencies of the first two are
-    // fetched once, before any row load; fetched inside the table phase, each
-    // entry's load waited for the row's loads and for the entry before it.
-    // Narrower rows (one entry per lane and token) keep the round-robin
-    // spread, which holds no registers across the row loop.
-    constexpr bool kHoist = !TRAD && !MASKED && VPT * LPR * VEC > 128;
+    // Split-half kernels fetch a lane's inverse frequencies once, before any
+    // row load, with the lane's pairs fixed (L, L + 64, ...): fetched inside
+    // the table phase, each entry's load waits for the row's loads and for
+    // the entry before it.  The fetched values stay in registers across the
+    // row loop, which pays where a lane has two or more entries per token
+    // (rows of more than 128 features) and where the kernel already holds
+    // enough registers that these cost no occupancy (two or more packs of
+    // 2-byte elements per lane).  Other kernels keep the round-robin spread.
+    constexpr bool kHoist =
+        !TRAD && !MASKED && (VPT * LPR * VEC > 128 || (VPT >= 2 && VEC == 8));
     double inv0 = 0.0, inv1 = 0.0;
     if constexpr (kHoist) {
         inv0 = wave_lane < ihalf ? inv_turns(wave_lane) : 0.0;
