@@ -171,6 +171,9 @@ bool rope_ok(const Variant& v, int64_t dims) {
     if (half % v.vec != 0) return false;
     const int64_t dp = half / v.vec;
     if (v.vpt == 1) return 2 * dp <= v.lpr;
+    // two packs per lane: full rotation only (the kernel has no code for a
+    // partial one there); more packs: whole packs of partners per lane
+    if (v.vpt == 2) return dp == v.lpr;
     return dp % v.lpr == 0;
 }
 

@@ -113,16 +113,14 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
     float2* wtab = cs + int64_t(wave) * W * half;
     const int ihalf = static_cast<int>(half);
 
-    // Split-half kernels fetch a lane's inverse frequencies once, before any
-    // row load, with the lane's pairs fixed (L, L + 64, ...): fetched inside
-    // the table phase, each entry's load waits for the row's loads and for
-    // the entry before it.  The fetched values stay in registers across the
-    // row loop, which pays where a lane has two or more entries per token
-    // (rows of more than 128 features) and where the kernel already holds
-    // enough registers that these cost no occupancy (two or more packs of
-    // 2-byte elements per lane).  Other kernels keep the round-robin spread.
-    constexpr bool kHoist =
-        !TRAD && !MASKED && (VPT * LPR * VEC > 128 || (VPT >= 2 && VEC == 8));
+    // Split-half rows of more than 128 features give a lane two or more
+    // table entries per token.  In those kernels a lane's pairs are fixed
+    // (L, L + 64, ...) and the inverse frequencies of the first two are
+    // fetched once, before any row load; fetched inside the table phase, each
+    // entry's load waited for the row's loads and for the entry before it.
+    // Narrower rows (one entry per lane and token) keep the round-robin
+    // spread, which holds no registers across the row loop.
+    constexpr bool kHoist = !TRAD && !MASKED && VPT * LPR * VEC > 128;
     double inv0 = 0.0, inv1 = 0.0;
     if constexpr (kHoist) {
         inv0 = wave_lane < ihalf ? inv_turns(wave_lane) : 0.0;
@@ -295,18 +293,21 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
                 // Pack v is rotated when v < 2 dv and pairs with pack v + dv
                 // (v < dv) or v - dv: conditions on v alone, uniform.
                 const int dv = int(dp / LPR);
-                if (2 * dv == VPT) {
-                    // every feature rotates: the pairing is known at compile time
-                    static_for<VPT>([&](auto vi) {
+                // With two packs per lane the host's shape rule leaves only
+                // full rotation (dv = 1), so those kernels carry no code for
+                // the partial case and its registers.
+                if (VPT == 2 || 2 * dv == VPT) {
+                    // every feature rotates: the pairing is known at compile
+                    // time; pack v < VPT/2 pairs with pack v + VPT/2 and both
+                    // rotate with the same table entries
+                    static_for<VPT / 2>([&](auto vi) {
                         constexpr int v = decltype(vi)::value;
-                        constexpr bool first = v < VPT / 2;
-                        constexpr int vp = first ? v + VPT / 2 : v - VPT / 2;
-                        constexpr int tv = first ? v : vp;
+                        constexpr int vp = v + VPT / 2;
 #pragma unroll
                         for (int i = 0; i < VEC; ++i) {
-                            const float2 t = tab[(tv * LPR + lane) * VEC + i];
-                            out[v][i] = first ? o[v][i] * t.x - o[vp][i] * t.y
-                                              : o[v][i] * t.x + o[vp][i] * t.y;
+                            const float2 t = tab[(v * LPR + lane) * VEC + i];
+                            out[v][i] = o[v][i] * t.x - o[vp][i] * t.y;
+                            out[vp][i] = o[vp][i] * t.x + o[v][i] * t.y;
                         }
                     });
                 } else {
