@@ -387,3 +387,21 @@ def test_prepare_rejects_host_tensors_and_restores_the_library():
     with pytest.raises(ValueError, match="GPU"):
         trn.prepare(trn.rms_norm, x, torch.ones(8), 1e-6)
     assert isinstance(trn.lib(), ctypes.CDLL)      # no recorder left behind
+
+
+def test_two_pack_rope_kernels_serve_full_rotation_only():
+    """Split-half kernels with two packs per lane carry no code for a partial
+    rotation: the host must never pick one for dims < head_dim.  Every
+    (type, head_dim, dims) the library serves is enumerated over every
+    variant it offers."""
+    import re
+    seen_two_pack = 0
+    for dt in (F32, BF16, trn.F16):
+        for hd in list(range(2, 258, 2)) + [384, 512, 640, 768, 1024, 2048]:
+            for dims in range(2, hd + 1, 2):
+                for v in range(trn.rope_variant_count(dt, hd, dims, False)):
+                    name = trn.describe_rope(dt, hd, dims, False, variant=v)
+                    if re.search(r"\.vpt2\.", name):
+                        seen_two_pack += 1
+                        assert dims == hd, (dt, hd, dims, name)
+    assert seen_two_pack > 0
