@@ -7,6 +7,54 @@
 
 namespace fnorm {
 
+// DPP rotation by 8 within a 16-lane row, and ds_swizzle's bitmask mode
+// for lane ^ 4 (and 0x1f, xor 0x04).
+constexpr int DPP_ROW_ROR8 = 0x128;   // lane l <- lane l ^ 8 (rotate by 8 of 16)
+constexpr int SWIZZLE_XOR4 = 0x101F;
+
+// Value of `v` held by the lane at distance D within the row group (the
+// split-half RoPE partner), D a compile-time distance: DPP for D = 1, 2, 8
+// (inside a 16-lane row), ds_swizzle for D = 4 and 16, and ds_bpermute from
+// `bperm_addr` (source lane * 4) for D = 0, meaning any other distance.  At
+// D = 4 one swizzle replaces two row shifts and a select (three VALU
+// instructions per element of a head_dim 64 row).
+template <int D>
+__device__ __forceinline__ float lane_partner(float v, int bperm_addr) {
+    if constexpr (D == 1) {
+        return dpp<DPP_QUAD_1032>(v);
+    } else if constexpr (D == 2) {
+        return dpp<DPP_QUAD_2301>(v);
+    } else if constexpr (D == 4) {
+        return __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), SWIZZLE_XOR4));
+    } else if constexpr (D == 8) {
+        return dpp<DPP_ROW_ROR8>(v);
+    } else if constexpr (D == 16) {
+        return __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), SWIZZLE_XOR16));
+    } else {
+        static_assert(D == 0, "partner distance");
+        return __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute(bperm_addr, __builtin_bit_cast(int, v)));
+    }
+}
+
+// Calls f(std::integral_constant<int, D>) with D the compile-time form of
+// the runtime partner distance d (0 for distances without a DPP/swizzle
+// pattern), so that the choice is one uniform branch per row, not one per
+// element.
+template <class F>
+__device__ __forceinline__ void with_partner_distance(int d, F&& f) {
+    switch (d) {
+        case 1: f(std::integral_constant<int, 1>{}); break;
+        case 2: f(std::integral_constant<int, 2>{}); break;
+        case 4: f(std::integral_constant<int, 4>{}); break;
+        case 8: f(std::integral_constant<int, 8>{}); break;
+        case 16: f(std::integral_constant<int, 16>{}); break;
+        default: f(std::integral_constant<int, 0>{}); break;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Dual q/k head RMSNorm fused with the rotary position embedding (RoPE) of
 // both outputs, one launch.  Norm definition as in fnorm_kernels.hpp; RoPE
@@ -279,7 +327,7 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
                     constexpr int D = decltype(dc)::value;
 #pragma unroll
                     for (int i = 0; i < VEC; ++i)
-                        q[i] = lane_partner<D>(o[0][i], wave_lane, src);
+                        q[i] = lane_partner<D>(o[0][i], src);
                 });
                 if (rot) {
 #pragma unroll
