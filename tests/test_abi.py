@@ -389,19 +389,28 @@ def test_prepare_rejects_host_tensors_and_restores_the_library():
     assert isinstance(trn.lib(), ctypes.CDLL)      # no recorder left behind
 
 
-def test_two_pack_rope_kernels_serve_full_rotation_only():
-    """Split-half kernels with two packs per lane carry no code for a partial
-    rotation: the host must never pick one for dims < head_dim.  Every
-    (type, head_dim, dims) the library serves is enumerated over every
-    variant it offers."""
+def test_multi_pack_rope_kernels_serve_only_their_pairings():
+    """Split-half kernels with two or four packs per lane carry compile-time
+    pairings only: two packs serve full rotation only (the partner pack one
+    away), four packs a partner one or two packs away.  Every (type,
+    head_dim, dims) the library serves is enumerated over every variant it
+    offers."""
     import re
-    seen_two_pack = 0
+    seen = {2: 0, 4: 0}
     for dt in (F32, BF16, trn.F16):
         for hd in list(range(2, 258, 2)) + [384, 512, 640, 768, 1024, 2048]:
             for dims in range(2, hd + 1, 2):
                 for v in range(trn.rope_variant_count(dt, hd, dims, False)):
                     name = trn.describe_rope(dt, hd, dims, False, variant=v)
-                    if re.search(r"\.vpt2\.", name):
-                        seen_two_pack += 1
+                    m = re.search(r"\.vec(\d+)\.vpt(\d+)\.lpr(\d+)\.", name)
+                    vec, vpt, lpr = map(int, m.groups())
+                    if vpt not in seen:
+                        continue
+                    seen[vpt] += 1
+                    dp = dims // 2 // vec          # partner distance in packs
+                    assert dp % lpr == 0, (dt, hd, dims, name)
+                    dv = dp // lpr                 # ... in packs of one lane
+                    assert dv == 1 if vpt == 2 else dv in (1, 2), (dt, hd, dims, name)
+                    if vpt == 2:
                         assert dims == hd, (dt, hd, dims, name)
-    assert seen_two_pack > 0
+    assert seen[2] > 0 and seen[4] > 0

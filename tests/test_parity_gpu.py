@@ -558,8 +558,8 @@ ROPE_CASES = [  # (dtype, tokens, q_heads, k_heads, head_dim, dims, traditional,
     (torch.bfloat16, 21, 4, 2, 256, 256, False, 10000.0, 1.0, 99, True),
     (torch.bfloat16, 15, 5, 3, 256, 192, False, 10000.0, 1.0, 4096, False),
     (torch.float32, 9, 3, 2, 256, 192, False, 10000.0, 1.0, 123, True),
-    # the head_dim 256 defaults: 2 packs in 16 lanes (split-half, fp16) and
-    # 4 packs in 8 lanes (interleaved)
+    # head_dim 256 in fp16 (split-half) and interleaved bf16: the 4- and
+    # 2-pack shapes run as variants of every case
     (torch.float16, 17, 6, 2, 256, 256, False, 10000.0, 1.0, 321, False),
     (torch.bfloat16, 19, 4, 2, 256, 256, True, 10000.0, 1.0, 55, False),
 ]

@@ -66,22 +66,19 @@ void register_rope_dtype(std::vector<Variant>& t) {
     // packs per lane, and 4 packs in 4 lanes at bf16 head_dim 128 were
     // slower (22.6 us).  Rows of 8 packs keep one pack per lane on a
     // persistent grid (34.7 against 37.2 us at 16384 tokens).
-    // Since the two-pack kernels compile full rotation only (69-80 VGPRs
-    // instead of 84-96), split-half rows of 32 two-byte packs run faster with
-    // 2 packs in 16 lanes than with 4 in 8: bf16 head_dim 256 30.2 against
-    // 31.3 us at 4096 tokens, 108.1 against 113.6 at 16384, 215.5 against
-    // 224.0 at 32768.  Interleaved pairs keep 4 packs in 8 lanes (31.4
-    // against 33.4 at 4096 tokens but 114.1 against 111.0 at 16384).
+    // With the split-half pairings of two- and four-pack rows fixed at
+    // compile time (69-80 and 127 VGPRs), 4 packs in 8 lanes stays the
+    // fastest for rows of 32 two-byte packs: bf16 head_dim 256 29.8 against
+    // 30.4 us for 2 packs in 16 lanes at 4096 tokens, 105.6 against 108.4 at
+    // 16384 (the plain dual: 30.2 and 113.0); head_dim 512 (4 in 16) 62.5
+    // against 63.8 for 2 in 32 at 4096 tokens, 226.3 against 239.9 at 16384.
     add_rope<DT, V, 1, 8, 256, false, NT_BOTH>(t);
     add_rope<DT, V, 2, 8, 256, false, NT_BOTH>(t, true);
     if constexpr (Elem<DT>::bytes == 2) {
-        t.push_back(make_rope<DT, V, 2, 16, 256, false, NT_BOTH, false>(true));
         add_rope<DT, V, 4, 8, 256, false, NT_BOTH>(t, true);
         add_rope<DT, V, 4, 16, 256, false, NT_BOTH>(t, true);
-        t.push_back(make_rope<DT, V, 2, 16, 256, false, NT_BOTH, true>(true));
-    } else {
-        add_rope<DT, V, 2, 16, 256, false, NT_BOTH>(t, true);
     }
+    add_rope<DT, V, 2, 16, 256, false, NT_BOTH>(t, true);
     add_rope<DT, V, 1, 16, 256, false, NT_BOTH>(t);
     add_rope<DT, V, 1, 16, 512, false, NT_BOTH>(t);
     add_rope<DT, V, 1, 16, 1024, false, NT_BOTH>(t);

@@ -342,8 +342,9 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
                 // (v < dv) or v - dv: conditions on v alone, uniform.
                 const int dv = int(dp / LPR);
                 // With two packs per lane the host's shape rule leaves only
-                // full rotation (dv = 1), so those kernels carry no code for
-                // the partial case and its registers.
+                // full rotation (dv = 1), and with four only dv = 1 or 2, so
+                // those kernels carry compile-time pairings and no code (or
+                // registers) for the general case.
                 if (VPT == 2 || 2 * dv == VPT) {
                     // every feature rotates: the pairing is known at compile
                     // time; pack v < VPT/2 pairs with pack v + VPT/2 and both
@@ -358,6 +359,16 @@ __global__ __launch_bounds__(BLOCK) void dual_rope_rows(RopeArgs ra) {
                             out[vp][i] = o[vp][i] * t.x + o[v][i] * t.y;
                         }
                     });
+                } else if constexpr (VPT == 4) {
+                    // four packs: the shape rule leaves dv = 2 (above) or
+                    // dv = 1, where packs 0 and 1 rotate as a pair and packs
+                    // 2 and 3 pass through
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) {
+                        const float2 t = tab[lane * VEC + i];
+                        out[0][i] = o[0][i] * t.x - o[1][i] * t.y;
+                        out[1][i] = o[1][i] * t.x + o[0][i] * t.y;
+                    }
                 } else {
 #pragma unroll
                     for (int v = 0; v < VPT; ++v) {
