@@ -201,8 +201,10 @@ def test_launch_policy_and_per_kind_order():
     # head vectors of 8-32 packs: exact shapes with non-temporal access on a plain grid
     assert trn.describe(trn.OP_DUAL, BF16, 64) == "dual.bf16.vec8.vpt1.lpr8.blk256.exact.nt.grid"
     assert trn.describe(trn.OP_DUAL, BF16, 128) == "dual.bf16.vec8.vpt2.lpr8.blk256.exact.nt.grid"
-    assert trn.describe(trn.OP_DUAL, BF16, 256) == "dual.bf16.vec8.vpt1.lpr32.blk256.exact.nt.grid"
-    assert trn.describe(trn.OP_DUAL, F32, 128) == "dual.f32.vec4.vpt1.lpr32.blk256.exact.nt.grid"
+    assert trn.describe(trn.OP_DUAL, BF16, 256) == "dual.bf16.vec8.vpt2.lpr16.blk256.exact.nt.grid"
+    assert trn.describe(trn.OP_DUAL, F32, 128) == "dual.f32.vec4.vpt2.lpr16.blk256.exact.nt.grid"
+    assert trn.describe(trn.OP_RMS_SWIGLU, BF16, 256) == \
+        "rmsgate.bf16.vec8.vpt1.lpr32.blk256.exact.nt.grid"
     assert trn.describe(trn.OP_DUAL, BF16, 192) == "dual.bf16.vec8.vpt3.lpr8.blk256.exact.nt.grid"
     assert trn.describe(trn.OP_LAYER, BF16, 576) == "layer.bf16.vec8.vpt9.lpr8.blk256.exact.nt.grid"
     assert trn.describe(trn.OP_LAYER, BF16, 640) == "layer.bf16.vec8.vpt5.lpr16.blk256.exact.nt.grid"

@@ -201,12 +201,19 @@ inline void register_dtype(std::vector<Variant>& t) {
     // tokens 97.3 against 81.5).  The same for 12 packs (3 in 4 lanes) was
     // 2-15% slower than the masked 16-lane shape.
     FNORM_EXACT(3, 8, 256, NT_BOTH, GRID_FIRST)
-    // 32 packs (bf16 256 / f32 128; dual at those head sizes: non-temporal
-    // stores 4-5% faster)
+    // 32 packs (bf16 256 / f32 128): 2 packs in 16 lanes with non-temporal
+    // loads and stores on a plain grid for RMSNorm, LayerNorm and the dual
+    // (bf16 head_dim 256: the dual 30.2 -> 28.3 us at 4096 tokens, 112.9 ->
+    // 104.5 at 16384; over 256 MiB LayerNorm 92.1 -> 84.3 us, RMSNorm 87.7 ->
+    // 84.0; fp32 128 3-5%).  The gated form keeps one pack in 32 lanes
+    // (121.6 against 126.9 us).  Non-temporal stores are 4-5% faster than
+    // ordinary ones for the dual at these head sizes.
+    FNORM_EXACT_FOR(KM_LAYER | (1u << K_RMS) | (1u << K_DUAL), 2, 16, 256, NT_BOTH, GRID_FIRST)
     FNORM_EXACT(1, 32, 256, NT_BOTH, GRID_FIRST)
     FNORM_EXACT(1, 32, 256, NT_LOAD, 0)
     FNORM_EXACT(2, 16, 256, NT_NONE, 0)
     FNORM_EXACT(1, 32, 256, NT_NONE, 0)
+    FNORM_EXACT_FOR(1u << K_RMS_GATED, 2, 16, 256, NT_BOTH, GRID_FIRST)
     // 72 and 80 packs (bf16 576 and 640, fp32 288 and 320): 9 packs in 8
     // lanes and 5 in 16 on a plain grid, LayerNorm 7-16% faster than the
     // masked 64-lane shape the rows only partly fill (bf16 576: 102.9
