@@ -189,7 +189,9 @@ VARIANT_CASES = [("rms", torch.bfloat16, 128), ("rms", torch.bfloat16, 768),
                  ("layer", torch.bfloat16, 192), ("rms", torch.float32, 96),
                  ("layer", torch.bfloat16, 576), ("layer", torch.float32, 320),
                  ("rms", torch.bfloat16, 576), ("rms", torch.bfloat16, 640),
-                 ("rms", torch.float32, 288), ("rms", torch.bfloat16, 192)]
+                 ("rms", torch.float32, 288), ("rms", torch.bfloat16, 192),
+                 ("layer", torch.bfloat16, 256), ("layer", torch.float32, 128),
+                 ("rms", torch.float16, 256)]
 
 
 @pytest.mark.parametrize("op,dtype,width", VARIANT_CASES,
