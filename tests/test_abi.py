@@ -336,6 +336,24 @@ def test_packed_qkv_layout_is_accepted(lib):
     assert lib.fnorm_last_error().startswith(b"fnorm_dual_head_rms_rope_strided: ")
 
 
+def test_dual_heads_times_head_dim_overflow_without_tokens(lib):
+    # no tokens: the row count is 0 and bounds nothing, so heads * head_dim
+    # itself is checked before any stride is formed from it
+    D, E = 0x1000000, 0x2000000
+    huge = 1 << 60
+    assert lib.fnorm_dual_head_rms_strided(A, 0, B, 0, D, E, C, 0, C + 64, 0, 0, huge, 1,
+                                           1 << 10, 1e-6, BF16, None, -1) == 2
+    assert b"overflows" in lib.fnorm_last_error()
+    assert lib.fnorm_dual_head_rms_strided(A, 0, B, 0, D, E, C, 0, C + 64, 0, 0, 1, huge,
+                                           1 << 10, 1e-6, BF16, None, -1) == 2
+    assert lib.fnorm_dual_head_rms_rope_strided(A, 0, B, 0, D, E, C, 0, C + 64, 0, 0, huge, 1,
+                                                1 << 10, 1e-6, 64, 0, 10000.0, 1.0, 0, None,
+                                                BF16, None, -1) == 2
+    # a shape that fits stays a no-op
+    assert lib.fnorm_dual_head_rms_strided(None, 0, None, 0, None, None, None, 0, None, 0, 0, 32,
+                                           8, 128, 1e-6, BF16, None, -1) == 0
+
+
 def test_rms_swiglu_validation(lib):
     G = 0x60000000
     # (x, g, w, y, rows, width, eps, dtype, stream, variant)

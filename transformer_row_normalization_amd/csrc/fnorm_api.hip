@@ -597,6 +597,9 @@ int dual_checks(const char* op, const void* q, int64_t qs, const void* k, int64_
         (tokens > 0 && (q_heads + k_heads) > (INT64_MAX / 16) / tokens))
         return fail(FNORM_ERR_SHAPE, op, "tokens * heads overflows");
     if (int s = check_scalars(op, dtype, tokens * (q_heads + k_heads), head_dim, eps)) return s;
+    // with no tokens the row count above is 0 and bounds nothing
+    if (!product_fits(q_heads, head_dim) || !product_fits(k_heads, head_dim))
+        return fail(FNORM_ERR_SHAPE, op, "heads * head_dim overflows");
     const int64_t qext = q_heads * head_dim, kext = k_heads * head_dim;
     if (tokens > 1 && ((q_heads > 0 && (qs < qext || qys < qext)) ||
                        (k_heads > 0 && (ks < kext || kys < kext))))
