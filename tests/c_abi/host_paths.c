@@ -170,6 +170,16 @@ static void entry_points(void)
                                                      1e-6f, 128, 0, 10000.0f, 1.0f, 0, NULL,
                                                      FNORM_BF16, NULL),
            FNORM_ERR_SHAPE);
+    /* no tokens: heads * head_dim alone overflows */
+    EXPECT("dual overflow no tokens",
+           fnorm_dual_head_rms_strided(A, 0, D, 0, B, E, C, 0, F, 0, 0, INT64_MAX / 8, 1, 1024,
+                                       1e-6f, FNORM_BF16, NULL, -1),
+           FNORM_ERR_SHAPE);
+    EXPECT("rope overflow no tokens",
+           fnorm_dual_head_rms_rope_strided(A, 0, D, 0, B, E, C, 0, F, 0, 0, 1, INT64_MAX / 8,
+                                            1024, 1e-6f, 64, 0, 10000.0f, 1.0f, 0, NULL,
+                                            FNORM_BF16, NULL, -1),
+           FNORM_ERR_SHAPE);
     {
         char nb[64];
         EXPECT("describe dual overflow", fnorm_describe_dual(A, 0, D, 0, B, E, C, 0, F, 0, 1,
