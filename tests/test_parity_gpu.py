@@ -564,6 +564,11 @@ ROPE_CASES = [  # (dtype, tokens, q_heads, k_heads, head_dim, dims, traditional,
     # 2-pack shapes run as variants of every case
     (torch.float16, 17, 6, 2, 256, 256, False, 10000.0, 1.0, 321, False),
     (torch.bfloat16, 19, 4, 2, 256, 256, True, 10000.0, 1.0, 55, False),
+    # the largest rotation served: 2048 pairs at head_dim 4096 (one row per
+    # wavefront, an angle table that fills the 64 KB LDS limit; pairs past
+    # 256 take the step factors)
+    (torch.bfloat16, 5, 2, 1, 4096, 4096, False, 10000.0, 1.0, 300, False),
+    (torch.float16, 3, 2, 1, 4096, 4096, True, 500000.0, 1.0, 7, True),
 ]
 
 
