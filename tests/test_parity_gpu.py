@@ -423,7 +423,11 @@ def test_magnitude_range(o):
 
 
 def test_wide_rows(o):
-    for dtype, width in ((torch.float32, 40000), (torch.bfloat16, 70000), (torch.bfloat16, 65537)):
+    # widths past the register capacity (strided passes over the row), up to
+    # rows of about a million features (fp16 2^20 + 3, a ragged width: the
+    # scalar-access kernel, ~1000 steps of 1024 threads per pass)
+    for dtype, width in ((torch.float32, 40000), (torch.bfloat16, 70000), (torch.bfloat16, 65537),
+                         (torch.float16, (1 << 20) + 3)):
         for op in ("rms", "layer"):
             t = inputs.random_rows(op, 5, width, dtype, seed=width)
             say(f"[wide] {op} {dtype} width={width}")
