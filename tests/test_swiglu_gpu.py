@@ -57,8 +57,10 @@ def case(rows, width, dtype, seed, extremes=True):
     return t
 
 
+# up to rows past every type's register capacity (fp32 40000, all types at
+# 65537 and 70000), which take the strided wide kernel
 WIDTHS = [1, 3, 8, 64, 100, 128, 192, 256, 576, 640, 768, 1024, 2560, 4096, 5120, 8192,
-          20000]
+          20000, 40000, 65537, 70000]
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: str(d)[6:])
