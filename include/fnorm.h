@@ -125,7 +125,11 @@ int fnorm_rms_swiglu_strided(const void* x, int64_t x_stride, const void* g, int
  * k, ky: [k_rows, head_dim]; qw, kw: [head_dim], shared by all heads.
  * Results are bitwise equal to fnorm_rms(q, qw, qy, ...) followed by
  * fnorm_rms(k, kw, ky, ...) with the same eps.  Either row count may be 0
- * (its pointers may then be NULL).
+ * (its pointers may then be NULL).  head_dim: any value up to 8192; above
+ * that, 16-byte-aligned pointers and a multiple of the 16-byte pack (8
+ * elements of bf16 / fp16, 4 of fp32), up to 65536 (bf16, fp16) or 32768
+ * (fp32).  Other head sizes return FNORM_ERR_UNSUPPORTED (the row-wide
+ * fnorm_rms serves any width).
  */
 int fnorm_dual_head_rms(const void* q, const void* k, const void* qw, const void* kw, void* qy,
                         void* ky, int64_t q_rows, int64_t k_rows, int64_t head_dim, float eps,

@@ -434,3 +434,17 @@ def test_multi_pack_rope_kernels_serve_only_their_pairings():
                     if vpt == 2:
                         assert dims == hd, (dt, hd, dims, name)
     assert seen[2] > 0 and seen[4] > 0
+
+
+def test_dual_head_dim_limits():
+    """The dual serves any head_dim up to 8192, and 16-byte-pack multiples
+    with aligned pointers up to 65536 (2-byte types) / 32768 (fp32)."""
+    for dt, cap, pack in ((trn.BF16, 65536, 8), (trn.F16, 65536, 8), (trn.F32, 32768, 4)):
+        for hd in (1, 7, 100, 8191, 8192):
+            for aligned in (True, False):
+                assert trn.variant_count(trn.OP_DUAL, dt, hd, aligned=aligned) > 0, (dt, hd)
+        for hd in (8192 + pack, 16384, cap):
+            assert trn.variant_count(trn.OP_DUAL, dt, hd, aligned=True) > 0, (dt, hd)
+            assert trn.variant_count(trn.OP_DUAL, dt, hd, aligned=False) == 0, (dt, hd)
+        for hd in (8193, cap + pack, cap + 1):
+            assert trn.variant_count(trn.OP_DUAL, dt, hd, aligned=True) == 0, (dt, hd)
