@@ -30,7 +30,8 @@ sums of any kernel able to serve the width, taken from the kernel names):
          r_j is at least 2^-10 |r_j|); elsewhere |y - r| <= E_j (1 + 2^-8)
          + 2^-8 |r_j| (the bound plus the final rounding); relative error
          <= 2^-7 against max(|r_j|, 2^10 E_j)
-  fp16   the same with 2^-13 (and fp16's absolute half spacing 2^-25)
+  fp16   the same with 2^-13 (and fp16's absolute half spacing 2^-25), the
+         relative error against max(|r_j|, 2^13 E_j, 2^-14)
 Each check returns its ulp histograms (all outputs, and those under the
 ulp rule) so the tests can report them.
 """
@@ -353,8 +354,12 @@ def check(op: str, y: torch.Tensor, r: np.ndarray, w: torch.Tensor | None = None
                                f"allows more than an ulp: diff {diff[bad][:3]}, "
                                f"E {bound[bad][:3]}, r {r[bad][:3]}")
         tol = BF16_REL_TOL if bf else F16_REL_TOL
-        out["max_rel"] = float(np.max(rel_err(yd, r, np.maximum(bound / shift, spacing * 2))
-                                      [finite])) if r.size else 0.0
+        # as in the pointwise check: below fp16's smallest normal (2^-14) the
+        # spacing is a fixed 2^-24, so relative error is taken against 2^-14
+        # there (one subnormal step is 2^-10 of it); the ulp rule above
+        # covers that range exactly
+        rfloor = np.maximum(bound / shift, spacing * 2 if bf else F16_MIN_NORMAL)
+        out["max_rel"] = float(np.max(rel_err(yd, r, rfloor)[finite])) if r.size else 0.0
         assert out["max_rel"] <= tol, f"{label}: rel err {out['max_rel']:.3e}"
         out["max_ulp"] = worst
     out["max_ulp_all"] = int(ulps.max()) if r.size else 0

@@ -170,3 +170,26 @@ def test_kernel_depth_parses_names():
     assert helpers.kernel_depth("rms.f32.vec4.wide.blk1024.persistent", 40000) == 40 + 6 + 15
     assert helpers.kernel_depth("layer.bf16.vec1.vpt4.lpr1024.blk1024.masked.persistent", 4096) \
         == 4 + 6 + 15
+
+
+
+def test_fp16_subnormal_outputs_under_the_bound_check():
+    """Below fp16's smallest normal (2^-14) the spacing is a fixed 2^-24, so
+    under 2^-15 even the correctly rounded value can be more than 2^-10 off
+    relatively (half a step of 2^-24 against |r| < 512 steps).  The bound
+    check takes relative error against 2^-14 there: the correctly rounded
+    value and its neighbour toward r pass (ulp distance 0 and 1), a value two
+    steps away fails."""
+    step = 2.0 ** -24
+    r = np.array([486.49 * step, -(300.45 * step), 1.5 + 0.49 * 2.0 ** -10])
+    bound = np.full(r.shape, 1e-12)               # the fp32 value is all but exact
+    rne = r.astype(np.float16).astype(np.float64)
+    spacing = np.where(np.abs(r) < 2.0 ** -14, step, 2.0 ** -10)   # 1.5 is in [1, 2)
+    toward = np.sign(r - rne)
+    for y, ulps in ((rne, 0), (rne + toward * spacing, 1)):
+        out = helpers.check("rms", torch.tensor(y, dtype=torch.float16), r, label=f"{ulps} ulp",
+                            bound=bound)
+        assert out["max_ulp"] == ulps and out["max_rel"] <= helpers.F16_REL_TOL
+    with pytest.raises(AssertionError):
+        helpers.check("rms", torch.tensor(rne + 2 * toward * spacing, dtype=torch.float16), r,
+                      label="two steps", bound=bound)
