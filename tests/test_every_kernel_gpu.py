@@ -154,3 +154,61 @@ def test_every_kernel(o, oname, dtype):
             expect = trn.describe(OPS[oname], code, width, aligned=aligned, variant=var)
             say(f"[every] {expect} width={width} aligned={aligned} variant={var}")
             run_one(o, oname, dtype, width, aligned, var, expect, seed=7 * i + var)
+
+
+def rope_kernels(code):
+    """Distinct fused RoPE kernels -> the first (head_dim, rotated dims,
+    interleaved, aligned, variant, count) that selects each."""
+    found = {}
+    for hd in range(2, 4097, 2):
+        for dims in sorted({hd, hd // 2 if (hd // 2) % 2 == 0 else hd, 2}):
+            for trad in (False, True):
+                for aligned in (True, False):
+                    try:
+                        n = trn.rope_variant_count(code, hd, dims, trad, aligned=aligned)
+                    except trn.FnormError:
+                        continue
+                    for v in range(n):
+                        name = trn.describe_rope(code, hd, dims, trad, aligned=aligned, variant=v)
+                        found.setdefault(name.rsplit(".", 1)[0], (hd, dims, trad, aligned, v, n))
+    return found
+
+
+@pytest.mark.parametrize("dtype", list(DTYPES), ids=["f32", "bf16", "f16"])
+def test_every_rope_kernel(o, dtype):
+    """Every fused RoPE kernel the dispatch can reach (head sizes 2-4096,
+    full, half and two-feature rotations, both pairings, aligned or not), in
+    both launch forms, against the oracle: 3 query + 1 key heads per token
+    at positions from 1000 on."""
+    code, _ = DTYPES[dtype]
+    found = rope_kernels(code)
+    assert found
+    say(f"[every-rope] {dtype}: {len(found)} kernels")
+    for i, (kern, (hd, dims, trad, aligned, v, n)) in enumerate(sorted(found.items(),
+                                                                     key=lambda kv: kv[1][0])):
+        for var in sorted({v, v ^ 1}):
+            if var >= n:
+                continue
+            expect = trn.describe_rope(code, hd, dims, trad, aligned=aligned, variant=var)
+            say(f"[every-rope] {expect} head_dim={hd} dims={dims} aligned={aligned} variant={var}")
+            rows = rows_for(expect, hd)
+            tokens = max(1, rows // 4)
+            g = torch.Generator().manual_seed(11 * i + var)
+            q = torch.randn(tokens, 3, hd, generator=g).to(dtype)
+            k = torch.randn(tokens, 1, hd, generator=g).to(dtype)
+            qw = (1 + 0.1 * torch.randn(hd, generator=g)).to(dtype)
+            kw = (1 + 0.1 * torch.randn(hd, generator=g)).to(dtype)
+            dq, dk, dqw, dkw = (placed(t, aligned) for t in (q, k, qw, kw))
+            qy, ky = empty_like_placed(q, aligned), empty_like_placed(k, aligned)
+            offset = 1000 + i
+            rope = {"dims": dims, "traditional": trad, "offset": offset}
+            got = trn.describe_dual_call(dq, dk, dqw, dkw, q_out=qy, k_out=ky, variant=var,
+                                         rope=rope)
+            assert got == expect, (got, expect)
+            trn.dual_head_rms_rope(dq, dk, dqw, dkw, 1e-6, dims=dims, traditional=trad,
+                                   offset=offset, q_out=qy, k_out=ky, variant=var)
+            torch.cuda.synchronize()
+            rq, rk = o.dual_head_rms_rope(*(helpers.to_oracle_array(t) for t in (q, k, qw, kw)),
+                                          1e-6, dims, trad, 10000.0, 1.0, offset)
+            helpers.check_rope(o, q, k, qw, kw, qy.cpu(), ky.cpu(), rq, rk, dims, trad,
+                               f"{expect} hd={hd}", (offset + tokens) / (2 * np.pi))
