@@ -7,8 +7,8 @@ aligned and not; each distinct kernel runs at the first width and alignment
 that selects it, on a ragged number of rows that spans several blocks of
 rows.  The call-level description (the library's own validation and choice
 for these tensors) confirms that the kernel under test is the one launched.
-The fused RoPE kernels have their own every-variant cases in
-test_parity_gpu.py."""
+The fused RoPE kernels get the same treatment over head sizes 2-4096 (full,
+half and two-feature rotations, both pairings)."""
 import sys
 
 import numpy as np
